@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Single-GPU benchmark of one GQA decode step (the split-K decode kernel + LSE merge).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one gqa_decode call over the whole batch of the workload, inputs resident in
+HBM. Several copies of the KV cache are rotated so that every step reads cold data
+(the 256 MiB Infinity Cache cannot serve a step from the previous one). Prints one
+JSON line:
+
+  value      KV GB/s = 2 * G * d_h * itemsize * sum(seq_lens) / (time per step)
+  roofline   the split-K decode kernel's own duration (HIP events on the launch
+             stream) against MI355X's 8 TB/s HBM peak
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GQA decode KV GB/s (% of MI355X HBM peak) and tokens/s at 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "gqa_internal.h")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gqa_kv_cache_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources (else null)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--policy", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--copies", type=int, default=0, help="KV cache copies rotated (0: enough for >= 1 GiB)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, budget_s: float):
+    """Time the oracle, as it is, on (sequence, KV group) units in order until the
+    budget is spent; report KV GB/s over the sample."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+    except Exception:  # pragma: no cover
+        threadpool_info = lambda: []
+    wl = inp.wl
+    hpg = wl.H // wl.G
+    done_bytes, elapsed, units = 0, 0.0, 0
+    for b in range(wl.B):
+        L = int(inp.lens[b])
+        for g in range(wl.G):
+            q = inp.q[b:b + 1, :, g * hpg:(g + 1) * hpg].float().cpu().numpy()
+            if inp.block_table is None:
+                k = inp.k_cache[b:b + 1, g:g + 1, :L].float().cpu().numpy()
+                v = inp.v_cache[b:b + 1, g:g + 1, :L].float().cpu().numpy()
+                tbl, P = None, 0
+            else:
+                import torch
+                P = wl.page_size
+                n = -(-L // P)
+                pages = torch.as_tensor(inp.table[b, :n].astype(np.int64), device=inp.k_cache.device)
+                k = inp.k_cache[pages][:, g:g + 1].float().cpu().numpy()
+                v = inp.v_cache[pages][:, g:g + 1].float().cpu().numpy()
+                tbl = np.arange(n, dtype=np.int64)[None, :]
+            t0 = time.perf_counter()
+            oracle.gqa_decode(q, k, v, inp.lens[b:b + 1], wl.scale, 1, block_table=tbl, page_size=P,
+                              causal=wl.causal)
+            elapsed += time.perf_counter() - t0
+            done_bytes += 2 * wl.d_h * wl.itemsize * L
+            units += 1
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    threads = 0
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 0)))
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        avail = os.cpu_count()
+    return {
+        "value": round(done_bytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads or avail,
+        "kind": "oracle",
+        "sample": (f"{units} of {wl.B * wl.G} (sequence, KV group) units, {elapsed:.1f} s of fp64 numpy "
+                   f"oracle time; {done_bytes / 1e6:.1f} MB of KV; host fp32 copies of the inputs, "
+                   f"upcast inside the timed region; {avail} cores visible"),
+        "tokens_per_s_equiv": round(units / (wl.B * wl.G) * wl.B * wl.q_len / elapsed, 3),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode step has no multi-GPU path in this build)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from gqa_kv_cache_03_amd import gqa_decode, plan, read_stream
+    from gqa_synth import BENCH_DEFAULT, make_inputs, workload
+
+    name = args.workload or BENCH_DEFAULT
+    wl = workload(name)
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    print(f"[bench] generating {name}", file=sys.stderr, flush=True)
+    inp = make_inputs(wl, device=dev)
+    kv_bytes = inp.kv_bytes
+    alloc_bytes = inp.k_cache.numel() * inp.k_cache.element_size() * 2
+    copies = args.copies or max(1, min(8, math.ceil((1 << 30) / alloc_bytes)))
+    ks, vs = [inp.k_cache], [inp.v_cache]
+    for _ in range(copies - 1):
+        ks.append(inp.k_cache.clone())
+        vs.append(inp.v_cache.clone())
+    out = torch.empty_like(inp.q)
+    kw = dict(scale=wl.scale, causal=wl.causal, num_splits=args.num_splits, chunk_tokens=args.chunk,
+              policy=args.policy)
+    pl = plan(inp.q, inp.k_cache, inp.block_table, causal=wl.causal, num_splits=args.num_splits,
+              chunk_tokens=args.chunk, policy=args.policy)
+    ws = torch.empty(max(pl["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
+
+    def step(i, events=None):
+        gqa_decode(inp.q, ks[i % copies], vs[i % copies], inp.seq_lens, inp.block_table, out=out,
+                   workspace=ws, profile_events=events, **kw)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] {args.steps} steps: {ms * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us)",
+          file=sys.stderr, flush=True)
+
+    # per-kernel durations: events recorded by the library around each launch
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for trio in evs:
+        for ev in trio:
+            ev.record()
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, events=[int(ev.cuda_event) for ev in evs[i]])
+    torch.cuda.synchronize()
+    dec = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
+    mrg = [evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)]
+    dec_ms = statistics.mean(dec)
+    mrg_ms = statistics.mean(mrg)
+
+    q_bytes = inp.q.numel() * inp.q.element_size()
+    tbl_bytes = 0 if inp.table is None else 4 * int(sum(-(-int(L) // wl.page_size) for L in inp.lens))
+    dec_alg_bytes = kv_bytes + q_bytes + tbl_bytes
+    achieved = dec_alg_bytes / (dec_ms * 1e-3) / 1e9
+
+    ceiling = None
+    if not args.no_ceiling:
+        buf = ks[0].view(torch.uint8).reshape(-1)
+        if buf.numel() < (1 << 30) and len(ks) > 1:
+            buf = torch.cat([k.view(torch.uint8).reshape(-1) for k in ks])
+        nbytes = buf.numel() // 16 * 16
+        sink = torch.empty(4096, dtype=torch.int32, device=dev)
+        read_stream(buf[:nbytes], sink)
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(5):
+            read_stream(buf[:nbytes], sink)
+        c1.record()
+        torch.cuda.synchronize()
+        ceiling = nbytes / (c0.elapsed_time(c1) / 5 * 1e-3) / 1e9
+        del buf
+
+    value = kv_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bfloat16" else "f32",
+        "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and block tables)",
+        "config": {
+            "workload": name,
+            "B": wl.B, "H": wl.H, "G": wl.G, "d_h": wl.d_h, "q_len": wl.q_len,
+            "layout": wl.layout, "page_size": wl.page_size or None,
+            "lengths": [wl.len_lo, wl.len_hi], "sum_seq_lens": int(inp.lens.sum()),
+            "kv_bytes": int(kv_bytes), "kv_copies_rotated": copies, "plan": pl,
+        },
+        "tokens_per_s": round(wl.B * wl.q_len / (ms * 1e-3), 1),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "read_ceiling_gbps": None if ceiling is None else round(ceiling, 1),
+        "kernel_ms": {"split_decode": round(dec_ms, 6), "lse_merge": round(mrg_ms, 6)},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": load_traffic(name),
+            "kernel": "decode_mfma_kernel" if pl["policy"] == "mfma" else "decode_valu_kernel",
+            "algorithmic_bytes_per_launch": int(dec_alg_bytes),
+        },
+        "cpu_baseline": None,
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 6),
+    }
+    del ks, vs
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

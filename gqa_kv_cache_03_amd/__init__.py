@@ -1,0 +1,8 @@
+"""MI355X (gfx950) grouped-query-attention decode: HIP kernels behind a C ABI.
+
+    from gqa_kv_cache_03_amd import gqa_decode
+    out = gqa_decode(q, k_cache, v_cache, seq_lens)            # contiguous cache
+    out = gqa_decode(q, pool_k, pool_v, seq_lens, block_table)  # paged cache
+"""
+from .ops import gqa_decode, plan, workspace_bytes, read_stream  # noqa: F401
+from ._lib import GqaError, LIB_PATH  # noqa: F401

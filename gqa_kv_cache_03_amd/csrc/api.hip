@@ -1,0 +1,245 @@
+// Host side of the C ABI: argument checks, launch planning and the two launches.
+//
+// Every check runs before any HIP call, so invalid calls return a status without
+// touching the device. The library holds no state and allocates nothing: split-K
+// partials go to the caller's workspace.
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/gqa_decode.h"
+#include "gqa_internal.h"
+
+namespace {
+
+using gqa::DecodeParams;
+
+constexpr int kMaxRows = 256;
+constexpr int kTargetSlots = 8192;   // split-kernel workgroup slots the heuristic aims for
+constexpr size_t kWsAlign = 256;
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int ilog2(int x) { int s = 0; while ((1 << s) < x) ++s; return s; }
+
+struct Plan {
+  gqa_plan pub;
+  bool paged;
+  int page_shift;
+  int row_block;
+  size_t ws_o_bytes;
+};
+
+int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* opts, bool paged,
+              Plan* out) {
+  if (!opts || opts->struct_size < sizeof(gqa_decode_opts)) return GQA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || G <= 0 || d_h <= 0 || q_len <= 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (G > H || H % G != 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (opts->dtype != GQA_DTYPE_F32 && opts->dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  if (d_h != 64 && d_h != 128) return GQA_ERR_UNSUPPORTED;
+  if (opts->causal != 0 && opts->causal != 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (opts->num_splits < 0 || opts->chunk_tokens < 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (opts->policy < GQA_POLICY_AUTO || opts->policy > GQA_POLICY_MFMA) return GQA_ERR_INVALID_ARGUMENT;
+
+  const int hpg = H / G;
+  const long long R = (long long)hpg * q_len;
+  if (R > kMaxRows) return GQA_ERR_UNSUPPORTED;
+  if ((long long)B * q_len * H > INT32_MAX / 256) return GQA_ERR_UNSUPPORTED;
+  if (B > 65535) return GQA_ERR_UNSUPPORTED;
+
+  Plan p{};
+  p.paged = paged;
+  int capacity;
+  if (paged) {
+    const int P = opts->page_size;
+    if (P < 16 || P > 256 || (P & (P - 1)) != 0) return GQA_ERR_INVALID_ARGUMENT;
+    if (opts->max_blocks_per_seq <= 0 || opts->num_pages <= 0) return GQA_ERR_INVALID_ARGUMENT;
+    if ((long long)opts->max_blocks_per_seq * P > INT32_MAX / 2) return GQA_ERR_UNSUPPORTED;
+    capacity = opts->max_blocks_per_seq * P;
+    p.page_shift = ilog2(P);
+  } else {
+    if (opts->cache_capacity <= 0) return GQA_ERR_INVALID_ARGUMENT;
+    capacity = opts->cache_capacity;
+  }
+  if (capacity < q_len) return GQA_ERR_INVALID_ARGUMENT;
+
+  int policy = opts->policy;
+  if (policy == GQA_POLICY_AUTO)
+    policy = (opts->dtype == GQA_DTYPE_BF16 && R >= 4) ? GQA_POLICY_MFMA : GQA_POLICY_VALU;
+  if (policy == GQA_POLICY_MFMA && opts->dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+
+  int tile, row_block = 1, n_rb = 1, lds;
+  if (policy == GQA_POLICY_MFMA) {
+    const gqa::MfmaVariant v = gqa::mfma_variant_for_rows((int)R, d_h);
+    tile = v.tile;
+    lds = v.lds_bytes;
+  } else {
+    row_block = R >= 8 ? 8 : (R >= 4 ? 4 : (R >= 2 ? 2 : 1));
+    n_rb = (int)((R + row_block - 1) / row_block);
+    tile = gqa::valu_tile_tokens(opts->dtype, d_h);
+    lds = gqa::valu_lds_bytes(opts->dtype, d_h, row_block);
+  }
+  if ((long long)G * n_rb > 65535) return GQA_ERR_UNSUPPORTED;
+
+  const long long cap_tiles = ((long long)capacity + tile - 1) / tile * tile;
+  long long chunk;
+  if (opts->chunk_tokens > 0) {
+    chunk = ((long long)opts->chunk_tokens + tile - 1) / tile * tile;
+  } else if (opts->num_splits > 0) {
+    const long long per = ((long long)capacity + opts->num_splits - 1) / opts->num_splits;
+    chunk = (per + tile - 1) / tile * tile;
+  } else {
+    // Enough workgroup slots to balance ragged lengths over 256 CUs, but keep each
+    // split long enough that its fp32 partials (R rows) stay small next to its KV
+    // bytes and its pipeline prologue is amortised.
+    const long long units = (long long)B * G * n_rb;
+    long long par = (long long)capacity * units / kTargetSlots;
+    long long lo = 4LL * tile;
+    if (16 * R > lo) lo = 16 * R;
+    chunk = par > lo ? par : lo;
+    chunk = (chunk + tile - 1) / tile * tile;
+  }
+  if (chunk > cap_tiles) chunk = cap_tiles;
+  if (chunk < tile) chunk = tile;
+  const long long splits = ((long long)capacity + chunk - 1) / chunk;
+  if (splits > INT32_MAX / 2) return GQA_ERR_UNSUPPORTED;
+
+  gqa_plan& pub = p.pub;
+  pub.policy = policy;
+  pub.rows = (int)R;
+  pub.row_blocks = n_rb;
+  pub.tile_tokens = tile;
+  pub.chunk_tokens = (int)chunk;
+  pub.max_splits = (int)splits;
+  pub.capacity = capacity;
+  pub.grid[0] = (int)splits;
+  pub.grid[1] = G * n_rb;
+  pub.grid[2] = B;
+  pub.block_threads = 256;
+  pub.lds_bytes = lds;
+  p.row_block = row_block;
+  if (splits > 1) {
+    const size_t rows = (size_t)B * q_len * H * (size_t)splits;
+    p.ws_o_bytes = round_up(rows * d_h * sizeof(float), kWsAlign);
+    pub.workspace_bytes = p.ws_o_bytes + round_up(rows * sizeof(float), kWsAlign);
+  } else {
+    p.ws_o_bytes = 0;
+    pub.workspace_bytes = 0;
+  }
+  *out = p;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void gqa_decode_opts_init(gqa_decode_opts* opts) {
+  if (!opts) return;
+  std::memset(opts, 0, sizeof(*opts));
+  opts->struct_size = sizeof(gqa_decode_opts);
+  opts->dtype = GQA_DTYPE_BF16;
+  opts->causal = 1;
+  opts->policy = GQA_POLICY_AUTO;
+}
+
+int gqa_abi_version(void) { return GQA_ABI_VERSION; }
+
+const char* gqa_status_string(int status) {
+  switch (status) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GQA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case GQA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int gqa_decode_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* opts,
+                    gqa_plan* plan) {
+  if (!plan || !opts) return GQA_ERR_INVALID_ARGUMENT;
+  Plan p;
+  const bool paged = opts->struct_size >= sizeof(gqa_decode_opts) && opts->page_size > 0;
+  const int st = make_plan(B, H, G, d_h, q_len, opts, paged, &p);
+  if (st != GQA_OK) return st;
+  *plan = p.pub;
+  return GQA_OK;
+}
+
+int gqa_decode_workspace_size(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* opts,
+                              size_t* bytes) {
+  if (!bytes) return GQA_ERR_INVALID_ARGUMENT;
+  gqa_plan plan;
+  const int st = gqa_decode_plan(B, H, G, d_h, q_len, opts, &plan);
+  if (st != GQA_OK) return st;
+  *bytes = plan.workspace_bytes;
+  return GQA_OK;
+}
+
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+               const int32_t* block_table, void* out, int B, int H, int G, int d_h, int q_len,
+               float scale, void* stream, const gqa_decode_opts* opts) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !out || !opts) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(seq_lens, 4) || (block_table && !aligned(block_table, 4)))
+    return GQA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+  Plan p;
+  const int st = make_plan(B, H, G, d_h, q_len, opts, block_table != nullptr, &p);
+  if (st != GQA_OK) return st;
+  if (!block_table && opts->page_size != 0) return GQA_ERR_INVALID_ARGUMENT;
+  const gqa_plan& pl = p.pub;
+  if (pl.max_splits > 1) {
+    if (!opts->workspace || !aligned(opts->workspace, kWsAlign) ||
+        opts->workspace_bytes < pl.workspace_bytes)
+      return GQA_ERR_WORKSPACE;
+  }
+
+  DecodeParams dp{};
+  dp.q = q;
+  dp.k = k_cache;
+  dp.v = v_cache;
+  dp.seq_lens = seq_lens;
+  dp.table = block_table;
+  dp.out = out;
+  if (pl.max_splits > 1) {
+    dp.ws_o = static_cast<float*>(opts->workspace);
+    dp.ws_lse = reinterpret_cast<float*>(static_cast<unsigned char*>(opts->workspace) + p.ws_o_bytes);
+  }
+  dp.B = B;
+  dp.H = H;
+  dp.G = G;
+  dp.q_len = q_len;
+  dp.hpg = H / G;
+  dp.R = pl.rows;
+  dp.capacity = pl.capacity;
+  dp.page_shift = p.paged ? p.page_shift : 0;
+  dp.max_blocks = p.paged ? opts->max_blocks_per_seq : 0;
+  dp.num_pages = p.paged ? opts->num_pages : 0;
+  dp.chunk = pl.chunk_tokens;
+  dp.max_splits = pl.max_splits;
+  dp.causal = opts->causal;
+  dp.row_block = p.row_block;
+  dp.n_row_blocks = pl.row_blocks;
+  dp.qk_scale_log2 = scale * 1.4426950408889634f;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(opts->profile_events));
+  if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return GQA_ERR_HIP;
+  const dim3 grid(pl.grid[0], pl.grid[1], pl.grid[2]);
+  hipError_t e = (pl.policy == GQA_POLICY_MFMA)
+                     ? gqa::launch_decode_mfma(dp, opts->dtype, d_h, p.paged, grid, s)
+                     : gqa::launch_decode_valu(dp, opts->dtype, d_h, p.paged, grid, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return GQA_ERR_HIP;
+  if (pl.max_splits > 1) {
+    e = gqa::launch_merge(dp, opts->dtype, d_h, s);
+    if (e != hipSuccess) return GQA_ERR_HIP;
+  }
+  if (ev[2] && hipEventRecord(ev[2], s) != hipSuccess) return GQA_ERR_HIP;
+  return GQA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal declarations shared by the host planner and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// Everything a split-K decode kernel needs; passed by value as the kernel argument.
+struct DecodeParams {
+  const void* q;           // [B, q_len, H, D]
+  const void* k;           // contiguous [B, G, cap, D] or paged [pages, G, P, D]
+  const void* v;
+  const int32_t* seq_lens; // [B]
+  const int32_t* table;    // [B, max_blocks] or nullptr
+  void* out;               // [B, q_len, H, D]
+  float* ws_o;             // [B, q_len, H, max_splits, D] fp32 (split partials, normalised)
+  float* ws_lse;           // [B, q_len, H, max_splits] fp32, log2-domain log-sum-exp
+  int B, H, G, q_len;
+  int hpg;                 // H / G
+  int R;                   // hpg * q_len packed rows per group
+  int capacity;            // tokens addressable per sequence
+  int page_shift;          // log2(page size) when paged
+  int max_blocks;          // block table row stride
+  int num_pages;
+  int chunk;               // tokens per split (multiple of the kernel tile)
+  int max_splits;
+  int causal;
+  int row_block;           // rows per workgroup along grid.y (VALU policy)
+  int n_row_blocks;
+  float qk_scale_log2;     // scale * log2(e): logits in base-2 units
+};
+
+// Row r of the packed group tile is query token t = r / hpg of head g*hpg + r % hpg.
+
+// Launchers (defined next to their kernels). Return hipSuccess or the launch error.
+hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int d_h, bool paged,
+                              dim3 grid, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int d_h, bool paged,
+                              dim3 grid, hipStream_t stream);
+hipError_t launch_merge(const DecodeParams& p, int dtype, int d_h, hipStream_t stream);
+
+// Static geometry of the MFMA kernel variants, chosen by packed row count R.
+struct MfmaVariant {
+  int max_rows;    // R this variant serves (multiple of 16)
+  int tile;        // keys per pipeline step
+  int lds_bytes;   // dynamic LDS per workgroup (D = 128)
+};
+MfmaVariant mfma_variant_for_rows(int R, int d_h);
+int valu_tile_tokens(int dtype, int d_h);
+int valu_lds_bytes(int dtype, int d_h, int row_block);
+
+}  // namespace gqa

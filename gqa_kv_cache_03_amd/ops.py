@@ -1,0 +1,140 @@
+"""Python binding of the decode library: torch tensors in, the C ABI call, status out.
+
+torch supplies device memory and the current stream only; every step of the decode
+runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+from . import _lib
+from ._lib import DecodeOpts, GqaError, Plan
+
+_POLICIES = {"auto": _lib.GQA_POLICY_AUTO, "valu": _lib.GQA_POLICY_VALU, "mfma": _lib.GQA_POLICY_MFMA}
+
+
+def _dtype_code(torch, dt) -> int:
+    if dt == torch.float32:
+        return _lib.GQA_DTYPE_F32
+    if dt == torch.bfloat16:
+        return _lib.GQA_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {dt}; float32 or bfloat16")
+
+
+def make_opts(*, dtype_code: int, causal: bool, capacity: int, page_size: int = 0,
+              max_blocks: int = 0, num_pages: int = 0, num_splits: int = 0,
+              chunk_tokens: int = 0, policy: str = "auto") -> DecodeOpts:
+    o = _lib.default_opts()
+    o.dtype = dtype_code
+    o.causal = 1 if causal else 0
+    o.cache_capacity = capacity
+    o.page_size = page_size
+    o.max_blocks_per_seq = max_blocks
+    o.num_pages = num_pages
+    o.num_splits = num_splits
+    o.chunk_tokens = chunk_tokens
+    o.policy = _POLICIES[policy]
+    return o
+
+
+def _geometry(q, k_cache, block_table):
+    B, q_len, H, d = q.shape
+    if block_table is None:
+        if k_cache.dim() != 4 or k_cache.shape[0] != B or k_cache.shape[3] != d:
+            raise ValueError("contiguous cache must be [B, G, capacity, d_h]")
+        G, cap = k_cache.shape[1], k_cache.shape[2]
+        return B, q_len, H, d, G, dict(capacity=cap)
+    if k_cache.dim() != 4 or k_cache.shape[3] != d:
+        raise ValueError("paged pool must be [num_pages, G, page_size, d_h]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    num_pages, G, P = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    return B, q_len, H, d, G, dict(capacity=0, page_size=P, max_blocks=block_table.shape[1],
+                                   num_pages=num_pages)
+
+
+def plan(q, k_cache, block_table=None, *, causal=True, num_splits=0, chunk_tokens=0,
+         policy="auto") -> dict:
+    """What gqa_decode would launch for these tensors (no device work)."""
+    import torch
+    B, q_len, H, d, G, geo = _geometry(q, k_cache, block_table)
+    o = make_opts(dtype_code=_dtype_code(torch, q.dtype), causal=causal, num_splits=num_splits,
+                  chunk_tokens=chunk_tokens, policy=policy, **geo)
+    pl = Plan()
+    st = _lib.lib().gqa_decode_plan(B, H, G, d, q_len, ctypes.byref(o), ctypes.byref(pl))
+    if st != _lib.GQA_OK:
+        raise GqaError(st, "gqa_decode_plan")
+    return pl.as_dict()
+
+
+def gqa_decode(q, k_cache, v_cache, seq_lens, block_table=None, *, scale: Optional[float] = None,
+               out=None, causal: bool = True, num_splits: int = 0, chunk_tokens: int = 0,
+               policy: str = "auto", workspace=None, profile_events=None):
+    """One GQA decode step on the current HIP stream; returns `out`.
+
+    q [B, q_len, H, d_h]; k_cache/v_cache [B, G, cap, d_h] (contiguous) or
+    [num_pages, G, page_size, d_h] with block_table int32 [B, max_blocks];
+    seq_lens int32 [B] counting the q_len new tokens. scale defaults to 1/sqrt(d_h).
+    """
+    import torch
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache must share one dtype")
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    if block_table is not None and (block_table.dtype != torch.int32 or not block_table.is_contiguous()
+                                    or not block_table.is_cuda):
+        raise TypeError("block_table must be a contiguous int32 device tensor")
+    B, q_len, H, d, G, geo = _geometry(q, k_cache, block_table)
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have B entries")
+    code = _dtype_code(torch, q.dtype)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = make_opts(dtype_code=code, causal=causal, num_splits=num_splits, chunk_tokens=chunk_tokens,
+                  policy=policy, **geo)
+    L = _lib.lib()
+    need = ctypes.c_size_t(0)
+    st = L.gqa_decode_workspace_size(B, H, G, d, q_len, ctypes.byref(o), ctypes.byref(need))
+    if st != _lib.GQA_OK:
+        raise GqaError(st, "gqa_decode_workspace_size")
+    if need.value:
+        if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+            workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+        o.workspace = workspace.data_ptr()
+        o.workspace_bytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if profile_events is not None:
+        for i, ev in enumerate(profile_events):
+            o.profile_events[i] = ev
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = L.gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                      None if block_table is None else block_table.data_ptr(), out.data_ptr(),
+                      B, H, G, d, q_len, ctypes.c_float(scale), stream, ctypes.byref(o))
+    if st != _lib.GQA_OK:
+        raise GqaError(st)
+    return out
+
+
+def workspace_bytes(q, k_cache, block_table=None, **kw) -> int:
+    return plan(q, k_cache, block_table, **kw)["workspace_bytes"]
+
+
+def read_stream(buf, sink) -> None:
+    """Measurement helper: stream-read `buf` (a device tensor) once."""
+    import torch
+    st = _lib.lib().gqa_bench_read_stream(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                          torch.cuda.current_stream(buf.device).cuda_stream)
+    if st != _lib.GQA_OK:
+        raise GqaError(st, "gqa_bench_read_stream")

@@ -1,0 +1,31 @@
+/*
+ * gqa_bench.h -- measurement helpers shipped with the decode library.
+ *
+ * Not part of the attention method. The bandwidth-wall section of the llms.blog
+ * GQA/MQA page says decode is bound by reloading the KV cache from HBM each step, so
+ * the decode kernel is judged against what plain streaming reads achieve on the same
+ * device; this helper measures that ceiling.
+ */
+#ifndef GQA_BENCH_H
+#define GQA_BENCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * gqa_bench_read_stream -- read `bytes` bytes of device memory at `buf` (16-byte
+ * aligned, bytes a multiple of 16) with coalesced 16-byte loads and write one
+ * 32-bit checksum word per workgroup into `sink` (device, at least 4 * 4096 bytes)
+ * so the reads cannot be elided. Asynchronous on `stream` (hipStream_t).
+ * Returns a gqa_status (INVALID_ARGUMENT for NULL/misaligned pointers or sizes).
+ */
+int gqa_bench_read_stream(const void* buf, size_t bytes, void* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQA_BENCH_H */

@@ -1,0 +1,141 @@
+/*
+ * gqa_decode.h -- C ABI of the MI355X (gfx950) grouped-query-attention decode library.
+ *
+ * One call computes one attention layer's decode step for a batch of sequences:
+ * for every sequence b, new query token t and query head h,
+ *
+ *     out[b,t,h,:] = sum_j softmax_j( scale * <q[b,t,h,:], K[b,g(h),j,:]> ) * V[b,g(h),j,:]
+ *
+ * over the cache positions j the token may see, with g(h) = h / (H/G).
+ *
+ * Sources (page title, section):
+ *  - "Grouped-Query Attention (GQA) and Multi-Query Attention (MQA): Mathematical
+ *    Foundations ..." (llms.blog), "Multi-Query Attention (MQA)" > "Mathematical
+ *    Formulation": logits = einsum(bhnk,bmk->bhnm), weights = softmax(logits + mask),
+ *    O = einsum(bhnm,bmv->bhnv); "Grouped-Query Attention (GQA)" > "Mathematical
+ *    Formulation": each group's key/value head is broadcast to its H/G query heads,
+ *    cache shape [b, G, m, d_k]; "PagedAttention": fixed-size token blocks.
+ *  - "Grouped-Query Attention" (aiwiki), the PyTorch listing: repeat_interleave of the
+ *    KV heads (contiguous head groups) and scaled_dot_product_attention with is_causal;
+ *    the note after it: the kernel derives the KV head from the query head and reads
+ *    the cache once instead of copying it. "Interaction with the cache": a page is
+ *    shared by the h/g query heads of its group.
+ *
+ * Conventions shared by every entry point:
+ *  - Return value: a gqa_status (0 = success). Nothing is thrown or aborted across
+ *    the ABI. Every argument check runs on the host before any HIP call.
+ *  - Device arrays are row-major, contiguous, 16-byte aligned, owned by the caller.
+ *  - The library keeps no state between calls and never allocates memory.
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_ABI_VERSION 1
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARGUMENT = 1, /* a NULL/misaligned pointer, a bad size, H % G != 0 ... */
+  GQA_ERR_UNSUPPORTED = 2,      /* valid but not compiled: d_h not 64/128, R > 256, ... */
+  GQA_ERR_WORKSPACE = 3,        /* the plan needs split-K scratch the caller did not give */
+  GQA_ERR_HIP = 4               /* a HIP launch or event call failed */
+} gqa_status;
+
+typedef enum gqa_dtype { GQA_DTYPE_F32 = 0, GQA_DTYPE_BF16 = 1 } gqa_dtype;
+
+/* Inner-product policy. AUTO: bf16 groups of R >= 4 packed query rows run QK^T and PV
+ * on MFMA (the packed rows make them dense contractions), everything else on the
+ * vector ALUs. The other values force one policy (tests, measurement). */
+typedef enum gqa_policy { GQA_POLICY_AUTO = 0, GQA_POLICY_VALU = 1, GQA_POLICY_MFMA = 2 } gqa_policy;
+
+typedef struct gqa_decode_opts {
+  uint32_t struct_size;       /* = sizeof(gqa_decode_opts); smaller values are rejected */
+  int32_t  dtype;             /* gqa_dtype of q, k_cache, v_cache and out */
+  int32_t  causal;            /* 1: token t of q_len sees keys 0 .. L-q_len+t; 0: all L keys */
+  int32_t  cache_capacity;    /* contiguous: token stride m of [B,G,m,d_h]; ignored if paged */
+  int32_t  page_size;         /* paged: tokens per page, a power of two in [16, 256] */
+  int32_t  max_blocks_per_seq;/* paged: row stride of block_table */
+  int32_t  num_pages;         /* paged: pages in the pool (entries are clamped to it) */
+  int32_t  num_splits;        /* 0: library heuristic; n > 0: at most n context splits */
+  int32_t  chunk_tokens;      /* 0: from num_splits/heuristic; else tokens per split
+                                 (rounded up to the kernel's tile) */
+  int32_t  policy;            /* gqa_policy */
+  void*    workspace;         /* device scratch for split-K partials (caller-owned) */
+  size_t   workspace_bytes;
+  void*    profile_events[3]; /* optional hipEvent_t: recorded on `stream` before the
+                                 split kernel, between it and the merge, after the merge */
+} gqa_decode_opts;
+
+/* What the library will launch for a shape (host-only, no HIP call). */
+typedef struct gqa_plan {
+  int32_t policy;             /* GQA_POLICY_VALU or GQA_POLICY_MFMA */
+  int32_t rows;               /* R = (H/G) * q_len query rows per KV group */
+  int32_t row_blocks;         /* workgroups that share one (b, g, split) along rows */
+  int32_t tile_tokens;        /* keys staged per pipeline step */
+  int32_t chunk_tokens;       /* keys per context split */
+  int32_t max_splits;         /* ceil(capacity / chunk_tokens) */
+  int32_t capacity;           /* tokens addressable per sequence */
+  int32_t grid[3];            /* split kernel grid (splits, G*row_blocks, B) */
+  int32_t block_threads;
+  int32_t lds_bytes;
+  size_t  workspace_bytes;    /* 0 when max_splits == 1 (the split kernel writes out) */
+} gqa_plan;
+
+/* Fill *opts with defaults: struct_size set, bf16, causal, heuristic splits, AUTO. */
+void gqa_decode_opts_init(gqa_decode_opts* opts);
+
+/*
+ * gqa_decode -- one decode step of grouped-query attention (asynchronous on `stream`).
+ *
+ *   q            [B, q_len, H, d_h]  queries of the q_len new tokens (dtype)
+ *   k_cache      contiguous: [B, G, cache_capacity, d_h]
+ *                paged (block_table != NULL): pool [num_pages, G, page_size, d_h]
+ *   v_cache      same layout as k_cache
+ *   seq_lens     int32 [B]: visible keys of sequence b, counting the q_len new tokens,
+ *                whose K/V the caller has already written. Precondition (not checked,
+ *                it lives on the device): q_len <= seq_lens[b] <= capacity. Values
+ *                outside are clamped to [1, capacity]; the result is then unspecified.
+ *   block_table  NULL for a contiguous cache, else int32 [B, max_blocks_per_seq]:
+ *                entry k is the pool page holding tokens [k*P, (k+1)*P) of sequence b.
+ *                Only entries below ceil(seq_lens[b]/P) are read.
+ *   out          [B, q_len, H, d_h] (dtype); fully overwritten, must not alias inputs.
+ *                bf16 results are rounded to nearest-even from fp32.
+ *   B, H, G      batch, query heads, KV heads: 1 <= G <= H, H % G == 0
+ *   d_h          head dimension: 64 or 128
+ *   q_len        new tokens per sequence (>= 1)
+ *   scale        logit scale, applied as given (1/sqrt(d_h) is the SDPA default)
+ *   stream       hipStream_t (NULL = default stream)
+ *   opts         required; see gqa_decode_opts
+ *
+ * Errors: INVALID_ARGUMENT for NULL or misaligned pointers, non-positive sizes,
+ * H % G != 0, non-finite scale, a bad opts struct or paged geometry; UNSUPPORTED for
+ * d_h not in {64,128}, an unknown dtype, R = (H/G)*q_len > 256 or a forced MFMA
+ * policy with fp32; WORKSPACE when more than one split is planned and workspace is
+ * NULL, too small or not 256-byte aligned; HIP when a launch fails.
+ */
+int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* seq_lens, const int32_t* block_table, void* out,
+               int B, int H, int G, int d_h, int q_len, float scale,
+               void* stream, const gqa_decode_opts* opts);
+
+/* The plan gqa_decode would use for these sizes (validation included). */
+int gqa_decode_plan(int B, int H, int G, int d_h, int q_len,
+                    const gqa_decode_opts* opts, gqa_plan* plan);
+
+/* Workspace bytes gqa_decode needs for these sizes (0 if none). */
+int gqa_decode_workspace_size(int B, int H, int G, int d_h, int q_len,
+                              const gqa_decode_opts* opts, size_t* bytes);
+
+const char* gqa_status_string(int status);
+int gqa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQA_DECODE_H */

@@ -1,0 +1,161 @@
+"""Host-side tests of the C ABI (no GPU needed: every check below returns before
+any HIP call). The library must load, export every declared symbol and reject bad
+arguments with the documented status codes."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from gqa_kv_cache_03_amd import _lib
+from gqa_kv_cache_03_amd._lib import DecodeOpts, Plan
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, INV, UNS, WS = (_lib.GQA_OK, _lib.GQA_ERR_INVALID_ARGUMENT, _lib.GQA_ERR_UNSUPPORTED,
+                    _lib.GQA_ERR_WORKSPACE)
+P = 4096  # a fake, aligned, non-null address: validation never dereferences it
+
+
+def declared_symbols():
+    names = set()
+    for h in ("gqa_decode.h", "gqa_bench.h"):
+        txt = open(os.path.join(ROOT, "include", h)).read()
+        txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+        for m in re.finditer(r"\b(?:int|void|size_t|const char\*)\s+(gqa_\w+)\s*\(", txt):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    decl = declared_symbols()
+    assert decl == set(_lib.EXPORTED)
+    for name in decl:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert decl <= exported
+
+
+def test_struct_layout_matches_header():
+    # struct_size, 9 int32 fields, pointer, size_t, 3 pointers
+    assert ctypes.sizeof(DecodeOpts) == 4 + 9 * 4 + 8 + 8 + 3 * 8
+    o = _lib.default_opts()
+    assert o.struct_size == ctypes.sizeof(DecodeOpts)
+    assert o.dtype == _lib.GQA_DTYPE_BF16 and o.causal == 1 and o.policy == 0
+    assert _lib.lib().gqa_abi_version() == 1
+
+
+def opts(**kw):
+    o = _lib.default_opts()
+    o.cache_capacity = 256
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return o
+
+
+def call(B=2, H=8, G=2, d=128, q_len=1, scale=0.1, o=None, q=P, k=P, v=P, sl=P, bt=None, out=P):
+    o = opts() if o is None else o
+    return _lib.lib().gqa_decode(q, k, v, sl, bt, out, B, H, G, d, q_len, ctypes.c_float(scale), None,
+                                 ctypes.byref(o) if o is not False else None)
+
+
+def plan(B=2, H=8, G=2, d=128, q_len=1, o=None):
+    o = opts() if o is None else o
+    pl = Plan()
+    st = _lib.lib().gqa_decode_plan(B, H, G, d, q_len, ctypes.byref(o), ctypes.byref(pl))
+    return st, pl
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INV), (dict(k=None), INV), (dict(v=None), INV), (dict(sl=None), INV), (dict(out=None), INV),
+    (dict(q=P + 8), INV), (dict(out=P + 4), INV), (dict(sl=P + 2), INV),
+    (dict(B=0), INV), (dict(H=0), INV), (dict(G=0), INV), (dict(d=0), INV), (dict(q_len=0), INV),
+    (dict(H=8, G=3), INV), (dict(H=4, G=8), INV),
+    (dict(scale=float("nan")), INV), (dict(scale=float("inf")), INV),
+    (dict(d=96), UNS), (dict(d=256), UNS),
+    (dict(H=64, G=1, q_len=5), UNS),                  # R = 320 > 256
+    (dict(o=False), INV),
+])
+def test_invalid_arguments_are_rejected(kw, status):
+    assert call(**kw) == status
+
+
+def test_opts_checks():
+    assert call(o=opts(struct_size=8)) == INV
+    assert call(o=opts(dtype=7)) == UNS
+    assert call(o=opts(causal=2)) == INV
+    assert call(o=opts(cache_capacity=0)) == INV
+    assert call(q_len=4, o=opts(cache_capacity=3)) == INV
+    assert call(o=opts(num_splits=-1)) == INV
+    assert call(o=opts(policy=9)) == INV
+    assert call(o=opts(dtype=_lib.GQA_DTYPE_F32, policy=_lib.GQA_POLICY_MFMA)) == UNS
+    assert call(o=opts(page_size=16)) == INV           # page size without a block table
+
+
+def test_paged_geometry_checks():
+    good = dict(page_size=16, max_blocks_per_seq=8, num_pages=40, num_splits=1)
+    assert call(bt=P, o=opts(**good)) != INV
+    for bad in (dict(page_size=0), dict(page_size=8), dict(page_size=24), dict(page_size=512),
+                dict(max_blocks_per_seq=0), dict(num_pages=0)):
+        assert call(bt=P, o=opts(**{**good, **bad})) == INV, bad
+    assert call(bt=P + 2, o=opts(**good)) == INV
+
+
+def test_workspace_required_when_split():
+    o = opts(num_splits=4)
+    assert call(o=o) == WS
+    st, pl = plan(o=o)
+    assert st == OK and pl.max_splits == 4 and pl.workspace_bytes > 0
+    o.workspace = 1000                                   # misaligned
+    o.workspace_bytes = pl.workspace_bytes
+    assert call(o=o) == WS
+    o.workspace = 4096
+    o.workspace_bytes = pl.workspace_bytes - 1
+    assert call(o=o) == WS
+
+
+def test_plan_policy_and_workspace_formula():
+    st, pl = plan(H=32, G=8, q_len=1, o=opts(cache_capacity=4096))
+    assert st == OK and pl.policy == _lib.GQA_POLICY_MFMA and pl.rows == 4
+    st, pl = plan(H=8, G=8, q_len=1, o=opts())                     # R = 1
+    assert pl.policy == _lib.GQA_POLICY_VALU and pl.rows == 1
+    st, pl = plan(H=8, G=2, o=opts(dtype=_lib.GQA_DTYPE_F32))
+    assert pl.policy == _lib.GQA_POLICY_VALU
+    # forced splits: chunk is ceil(cap / n) rounded up to the tile
+    st, pl = plan(B=3, H=16, G=4, q_len=2, o=opts(cache_capacity=1000, num_splits=3))
+    assert st == OK
+    assert pl.chunk_tokens % pl.tile_tokens == 0
+    assert pl.chunk_tokens >= -(-1000 // 3)
+    assert pl.max_splits == -(-1000 // pl.chunk_tokens) <= 3
+    rows = 3 * 2 * 16 * pl.max_splits
+    ro = lambda x: -(-x // 256) * 256
+    assert pl.workspace_bytes == ro(rows * 128 * 4) + ro(rows * 4)
+    assert list(pl.grid) == [pl.max_splits, 4, 3]
+    # single split needs no workspace
+    st, pl = plan(o=opts(num_splits=1))
+    assert pl.max_splits == 1 and pl.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 8, 16, 17, 32, 64, 65, 128, 256])
+def test_every_row_count_up_to_the_maximum_plans(R):
+    st, pl = plan(H=R, G=1, q_len=1, o=opts(cache_capacity=1 << 16))
+    assert st == OK and pl.rows == R
+    assert pl.policy == (_lib.GQA_POLICY_MFMA if R >= 4 else _lib.GQA_POLICY_VALU)
+    assert pl.lds_bytes <= 160 * 1024
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for s in range(5):
+        assert L.gqa_status_string(s)
+    assert L.gqa_status_string(99) == b"unknown status"
+
+
+def test_bench_helper_validation():
+    L = _lib.lib()
+    assert L.gqa_bench_read_stream(None, 16, P, None) == INV
+    assert L.gqa_bench_read_stream(P, 15, P, None) == INV
+    assert L.gqa_bench_read_stream(P + 4, 16, P, None) == INV
