@@ -62,6 +62,7 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--policy", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--staging", default="auto", choices=["auto", "dma", "regs"])
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies rotated (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -154,9 +155,9 @@ def main():
         vs.append(inp.v_cache.clone())
     out = torch.empty_like(inp.q)
     kw = dict(scale=wl.scale, causal=wl.causal, num_splits=args.num_splits, chunk_tokens=args.chunk,
-              policy=args.policy)
+              policy=args.policy, staging=args.staging)
     pl = plan(inp.q, inp.k_cache, inp.block_table, causal=wl.causal, num_splits=args.num_splits,
-              chunk_tokens=args.chunk, policy=args.policy)
+              chunk_tokens=args.chunk, policy=args.policy, staging=args.staging)
     ws = torch.empty(max(pl["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
 
     def step(i, events=None):
@@ -206,7 +207,7 @@ def main():
         if buf.numel() < (1 << 30) and len(ks) > 1:
             buf = torch.cat([k.view(torch.uint8).reshape(-1) for k in ks])
         nbytes = buf.numel() // 16 * 16
-        sink = torch.empty(4096, dtype=torch.int32, device=dev)
+        sink = torch.empty(8192, dtype=torch.int32, device=dev)
         read_stream(buf[:nbytes], sink)
         torch.cuda.synchronize()
         c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

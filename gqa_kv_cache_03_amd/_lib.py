@@ -47,6 +47,7 @@ class DecodeOpts(ctypes.Structure):
         ("num_splits", ctypes.c_int32),
         ("chunk_tokens", ctypes.c_int32),
         ("policy", ctypes.c_int32),
+        ("staging", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("profile_events", ctypes.c_void_p * 3),

@@ -30,6 +30,9 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
     # packed-FP32 (v_pk_*_f32) code generation stays off for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs (no AGPR copies around the
+    # per-step online-softmax rescale)
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -28,6 +28,7 @@ struct Plan {
   bool paged;
   int page_shift;
   int row_block;
+  int staging;
   size_t ws_o_bytes;
 };
 
@@ -41,6 +42,7 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
   if (opts->causal != 0 && opts->causal != 1) return GQA_ERR_INVALID_ARGUMENT;
   if (opts->num_splits < 0 || opts->chunk_tokens < 0) return GQA_ERR_INVALID_ARGUMENT;
   if (opts->policy < GQA_POLICY_AUTO || opts->policy > GQA_POLICY_MFMA) return GQA_ERR_INVALID_ARGUMENT;
+  if (opts->staging < 0 || opts->staging > 2) return GQA_ERR_INVALID_ARGUMENT;
 
   const int hpg = H / G;
   const long long R = (long long)hpg * q_len;
@@ -71,7 +73,9 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
 
   int tile, row_block = 1, n_rb = 1, lds;
   if (policy == GQA_POLICY_MFMA) {
-    const gqa::MfmaVariant v = gqa::mfma_variant_for_rows((int)R, d_h);
+    const int staging = opts->staging == 1 ? 0 : 1;  // default: register ring
+    const gqa::MfmaVariant v = gqa::mfma_variant_for_rows((int)R, d_h, staging);
+    p.staging = staging;
     tile = v.tile;
     lds = v.lds_bytes;
   } else {
@@ -223,6 +227,7 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const in
   dp.causal = opts->causal;
   dp.row_block = p.row_block;
   dp.n_row_blocks = pl.row_blocks;
+  dp.staging = p.staging;
   dp.qk_scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -12,24 +12,28 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
-constexpr int kBlocks = 4096;
+constexpr int kBlocks = 8192;
 constexpr int kThreads = 256;
-constexpr int kUnroll = 8;
+constexpr int kUnroll = 16;
 
-// Grid-stride over 16-byte words, kUnroll loads in flight per thread per round.
+// Each workgroup streams one contiguous slice with kUnroll nontemporal 16-byte loads in
+// flight per thread (the pattern that reached the highest rate in our measurements).
 __global__ __launch_bounds__(kThreads) void read_stream_kernel(const u32x4* __restrict__ buf, size_t n16,
                                                                uint32_t* __restrict__ sink) {
-  const size_t stride = (size_t)gridDim.x * kThreads;
-  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  constexpr size_t step = (size_t)kThreads * kUnroll;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per;
+  const size_t hi = lo + per < n16 ? lo + per : n16;
   uint32_t acc = 0;
-  for (; i + (kUnroll - 1) * stride < n16; i += kUnroll * stride) {
+  size_t base = lo;
+  for (; base + step <= hi; base += step) {
     u32x4 w[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) w[u] = buf[i + u * stride];
+    for (int u = 0; u < kUnroll; ++u) w[u] = __builtin_nontemporal_load(buf + base + u * kThreads + threadIdx.x);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= w[u][0] ^ w[u][1] ^ w[u][2] ^ w[u][3];
   }
-  for (; i < n16; i += stride) {
+  for (size_t i = base + threadIdx.x; i < hi; i += kThreads) {
     const u32x4 w = buf[i];
     acc ^= w[0] ^ w[1] ^ w[2] ^ w[3];
   }

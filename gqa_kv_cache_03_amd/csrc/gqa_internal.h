@@ -28,6 +28,7 @@ struct DecodeParams {
   int causal;
   int row_block;           // rows per workgroup along grid.y (VALU policy)
   int n_row_blocks;
+  int staging;             // MFMA kernel: 0 LDS-DMA ring, 1 register ring
   float qk_scale_log2;     // scale * log2(e): logits in base-2 units
 };
 
@@ -46,7 +47,7 @@ struct MfmaVariant {
   int tile;        // keys per pipeline step
   int lds_bytes;   // dynamic LDS per workgroup (D = 128)
 };
-MfmaVariant mfma_variant_for_rows(int R, int d_h);
+MfmaVariant mfma_variant_for_rows(int R, int d_h, int staging);
 int valu_tile_tokens(int dtype, int d_h);
 int valu_lds_bytes(int dtype, int d_h, int row_block);
 

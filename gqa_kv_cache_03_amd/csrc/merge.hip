@@ -8,6 +8,10 @@
 // (softmax of the llms.blog GQA/MQA page, "Multi-Query Attention" > "Mathematical
 // Formulation", evaluated piecewise). Splits past the sequence end were never
 // written and are not read; empty splits carry lse = -inf and weigh nothing.
+//
+// One 256-thread workgroup per output row (b, t, h). A split's D partial values are
+// read by D/4 lanes with 16-byte loads; the workgroup walks 4 * (256 / D) splits per
+// round, several rounds in flight per lane, and reduces across waves through LDS.
 
 #include "gqa_internal.h"
 
@@ -15,29 +19,35 @@ namespace gqa {
 namespace {
 
 constexpr float kNegInf = -__builtin_inff();
+constexpr int kThreads = 256;
 
-template <typename TT> __device__ __forceinline__ void put(TT* dst, float v);
-template <> __device__ __forceinline__ void put<float>(float* dst, float v) { *dst = v; }
-template <> __device__ __forceinline__ void put<__bf16>(__bf16* dst, float v) { *dst = (__bf16)v; }
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  return x;
+template <typename TT> __device__ __forceinline__ void put4(TT* dst, f32x4 v);
+template <> __device__ __forceinline__ void put4<float>(float* dst, f32x4 v) {
+  *reinterpret_cast<f32x4*>(dst) = v;
 }
-__device__ __forceinline__ float wave_sum(float x) {
+template <> __device__ __forceinline__ void put4<__bf16>(__bf16* dst, f32x4 v) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+  bf16x4 o;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  return x;
+  for (int i = 0; i < 4; ++i) o[i] = (__bf16)v[i];
+  *reinterpret_cast<bf16x4*>(dst) = o;
 }
 
-// One wave per output row (b, t, h); 4 rows per 256-thread workgroup.
 template <typename TT, int D>
-__global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int total_rows) {
-  constexpr int PER_LANE = D / 64;
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= total_rows) return;
+__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
+  constexpr int LPS = D / 4;                 // lanes per split row
+  constexpr int SPR = kThreads / LPS;        // splits per round (whole workgroup)
+  constexpr int U = 4;                       // rounds in flight per lane
+  __shared__ float red_m[kThreads / 64];
+  __shared__ f32x4 red_o[SPR][LPS];
+  __shared__ float red_w[SPR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int row = blockIdx.x;
   const int b = row / (p.q_len * p.H);
   int L = p.seq_lens[b];
   L = L < 1 ? 1 : (L > p.capacity ? p.capacity : L);
@@ -47,32 +57,61 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeParams p, int total_ro
   const float* lse = p.ws_lse + (size_t)row * p.max_splits;
   const float* po = p.ws_o + (size_t)row * p.max_splits * D;
 
+  // M = max over the row's splits
   float M = kNegInf;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, lse[s]);
-  M = wave_max(M);
+  for (int s = tid; s < ns; s += kThreads) M = fmaxf(M, lse[s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red_m[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   const float Mu = (M == kNegInf) ? 0.f : M;
 
-  float acc[PER_LANE];
-#pragma unroll
-  for (int i = 0; i < PER_LANE; ++i) acc[i] = 0.f;
+  // this thread: split slot sl = tid / LPS of every round, columns 4 * (tid % LPS)
+  const int sl = tid / LPS;
+  const int c = (tid % LPS) * 4;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = __builtin_amdgcn_exp2f(lse[s] - Mu);
-    wsum += w;
-    const float* src = po + (size_t)s * D + lane * PER_LANE;
+  for (int s0 = 0; s0 < ns; s0 += SPR * U) {
+    f32x4 v[U];
+    float w[U];
 #pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) acc[i] = fmaf(w, src[i], acc[i]);
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * SPR + sl;
+      if (s < ns) {
+        w[u] = __builtin_amdgcn_exp2f(lse[s] - Mu);
+        v[u] = *reinterpret_cast<const f32x4*>(po + (size_t)s * D + c);
+      } else {
+        w[u] = 0.f;
+        v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc += w[u] * v[u];
+      wsum += w[u];
+    }
   }
-  const float inv = (wsum > 0.f) ? 1.f / wsum : 0.f;
-  TT* dst = static_cast<TT*>(p.out) + (size_t)row * D + lane * PER_LANE;
+  red_o[sl][tid % LPS] = acc;
+  if (tid % LPS == 0) red_w[sl] = wsum;
+  __syncthreads();
+  if (tid < LPS) {
+    f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+    float wt = 0.f;
 #pragma unroll
-  for (int i = 0; i < PER_LANE; ++i) put<TT>(dst + i, acc[i] * inv);
+    for (int k = 0; k < SPR; ++k) {
+      tot += red_o[k][tid];
+      wt += red_w[k];
+    }
+    const float inv = (wt > 0.f) ? 1.f / wt : 0.f;
+    put4<TT>(static_cast<TT*>(p.out) + (size_t)row * D + tid * 4, tot * inv);
+  }
 }
 
 template <typename TT, int D>
 hipError_t go(const DecodeParams& p, hipStream_t stream) {
   const int total = p.B * p.q_len * p.H;
-  hipLaunchKernelGGL((merge_kernel<TT, D>), dim3((total + 3) / 4), dim3(256), 0, stream, p, total);
+  hipLaunchKernelGGL((merge_kernel<TT, D>), dim3(total), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

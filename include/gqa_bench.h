@@ -19,7 +19,7 @@ extern "C" {
 /*
  * gqa_bench_read_stream -- read `bytes` bytes of device memory at `buf` (16-byte
  * aligned, bytes a multiple of 16) with coalesced 16-byte loads and write one
- * 32-bit checksum word per workgroup into `sink` (device, at least 4 * 4096 bytes)
+ * 32-bit checksum word per workgroup into `sink` (device, at least 4 * 8192 bytes)
  * so the reads cannot be elided. Asynchronous on `stream` (hipStream_t).
  * Returns a gqa_status (INVALID_ARGUMENT for NULL/misaligned pointers or sizes).
  */

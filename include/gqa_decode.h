@@ -66,6 +66,8 @@ typedef struct gqa_decode_opts {
   int32_t  chunk_tokens;      /* 0: from num_splits/heuristic; else tokens per split
                                  (rounded up to the kernel's tile) */
   int32_t  policy;            /* gqa_policy */
+  int32_t  staging;           /* MFMA policy's K/V staging: 0 library choice, 1 direct
+                                 global->LDS ring, 2 register prefetch ring */
   void*    workspace;         /* device scratch for split-K partials (caller-owned) */
   size_t   workspace_bytes;
   void*    profile_events[3]; /* optional hipEvent_t: recorded on `stream` before the

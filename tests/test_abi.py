@@ -39,9 +39,33 @@ def test_library_exports_every_declared_symbol():
     assert decl <= exported
 
 
-def test_struct_layout_matches_header():
-    # struct_size, 9 int32 fields, pointer, size_t, 3 pointers
-    assert ctypes.sizeof(DecodeOpts) == 4 + 9 * 4 + 8 + 8 + 3 * 8
+def _c_offsets(tmp_path, struct, fields):
+    """offsetof() of each field, as the C compiler lays out the public header."""
+    src = tmp_path / "off.c"
+    body = "".join(f'  printf("%zu\\n", offsetof({struct}, {f}));\n' for f in fields)
+    src.write_text(f"""#include <stdio.h>
+#include <stddef.h>
+#include "gqa_decode.h"
+int main(void) {{
+  printf("%zu\\n", sizeof({struct}));
+{body}  return 0;
+}}
+""")
+    exe = tmp_path / "off"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    vals = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    return vals[0], vals[1:]
+
+
+@pytest.mark.parametrize("cls,struct", [(DecodeOpts, "gqa_decode_opts"), (Plan, "gqa_plan")])
+def test_struct_layout_matches_header(tmp_path, cls, struct):
+    fields = [f for f, _ in cls._fields_]
+    size, offs = _c_offsets(tmp_path, struct, fields)
+    assert ctypes.sizeof(cls) == size
+    assert [getattr(cls, f).offset for f in fields] == offs
+
+
+def test_default_opts():
     o = _lib.default_opts()
     assert o.struct_size == ctypes.sizeof(DecodeOpts)
     assert o.dtype == _lib.GQA_DTYPE_BF16 and o.causal == 1 and o.policy == 0
@@ -91,6 +115,7 @@ def test_opts_checks():
     assert call(q_len=4, o=opts(cache_capacity=3)) == INV
     assert call(o=opts(num_splits=-1)) == INV
     assert call(o=opts(policy=9)) == INV
+    assert call(o=opts(staging=3)) == INV
     assert call(o=opts(dtype=_lib.GQA_DTYPE_F32, policy=_lib.GQA_POLICY_MFMA)) == UNS
     assert call(o=opts(page_size=16)) == INV           # page size without a block table
 
