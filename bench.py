@@ -62,12 +62,25 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--policy", default="auto", choices=["auto", "valu", "mfma"])
-    ap.add_argument("--staging", default="auto", choices=["auto", "dma", "regs"])
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies rotated (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib: int) -> None:
+    """A plain device-to-device copy of known size, for scaling HBM byte counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
 
 
 def cpu_baseline(inp, budget_s: float):
@@ -134,6 +147,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the decode step has no multi-GPU path in this build)", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
     import numpy as np
     import torch
 
@@ -155,9 +171,9 @@ def main():
         vs.append(inp.v_cache.clone())
     out = torch.empty_like(inp.q)
     kw = dict(scale=wl.scale, causal=wl.causal, num_splits=args.num_splits, chunk_tokens=args.chunk,
-              policy=args.policy, staging=args.staging)
+              policy=args.policy)
     pl = plan(inp.q, inp.k_cache, inp.block_table, causal=wl.causal, num_splits=args.num_splits,
-              chunk_tokens=args.chunk, policy=args.policy, staging=args.staging)
+              chunk_tokens=args.chunk, policy=args.policy)
     ws = torch.empty(max(pl["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
 
     def step(i, events=None):

@@ -47,7 +47,6 @@ class DecodeOpts(ctypes.Structure):
         ("num_splits", ctypes.c_int32),
         ("chunk_tokens", ctypes.c_int32),
         ("policy", ctypes.c_int32),
-        ("staging", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("profile_events", ctypes.c_void_p * 3),
@@ -57,11 +56,13 @@ class DecodeOpts(ctypes.Structure):
 class Plan(ctypes.Structure):
     _fields_ = [
         ("policy", ctypes.c_int32),
+        ("schedule", ctypes.c_int32),
         ("rows", ctypes.c_int32),
         ("row_blocks", ctypes.c_int32),
         ("tile_tokens", ctypes.c_int32),
         ("chunk_tokens", ctypes.c_int32),
         ("max_splits", ctypes.c_int32),
+        ("workgroups", ctypes.c_int32),
         ("capacity", ctypes.c_int32),
         ("grid", ctypes.c_int32 * 3),
         ("block_threads", ctypes.c_int32),
@@ -72,11 +73,13 @@ class Plan(ctypes.Structure):
     def as_dict(self) -> dict:
         return {
             "policy": {1: "valu", 2: "mfma"}.get(self.policy, str(self.policy)),
+            "schedule": {0: "split-k grid", 1: "persistent balanced"}.get(self.schedule, str(self.schedule)),
             "rows": self.rows,
             "row_blocks": self.row_blocks,
             "tile_tokens": self.tile_tokens,
             "chunk_tokens": self.chunk_tokens,
             "max_splits": self.max_splits,
+            "workgroups": self.workgroups,
             "capacity": self.capacity,
             "grid": list(self.grid),
             "block_threads": self.block_threads,

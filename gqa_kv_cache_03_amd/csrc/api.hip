@@ -1,9 +1,11 @@
 // Host side of the C ABI: argument checks, launch planning and the two launches.
 //
-// Every check runs before any HIP call, so invalid calls return a status without
-// touching the device. The library holds no state and allocates nothing: split-K
-// partials go to the caller's workspace.
+// Every argument check runs before any HIP call, so invalid calls return a status
+// without touching the device. The library allocates nothing: split partials go to
+// the caller's workspace. The only state it keeps is a per-device cache of the CU
+// count (a read-only device property).
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -16,24 +18,47 @@ namespace {
 using gqa::DecodeParams;
 
 constexpr int kMaxRows = 256;
-constexpr int kTargetSlots = 8192;   // split-kernel workgroup slots the heuristic aims for
+constexpr int kTargetSlots = 8192;   // split-kernel workgroup slots the VALU heuristic aims for
 constexpr size_t kWsAlign = 256;
+constexpr int kMfmaTile = 32;        // keys per tile of the persistent MFMA schedule
+constexpr int kDefaultCUs = 256;     // MI355X, used when no device can be queried
+constexpr int kDefaultWgsPerCu = 2;
+constexpr int kMaxDevices = 64;
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline int ilog2(int x) { int s = 0; while ((1 << s) < x) ++s; return s; }
+
+// Compute units of the current device (cached per device; MI355X value without one).
+int device_cus() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  const int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 struct Plan {
   gqa_plan pub;
   bool paged;
   int page_shift;
   int row_block;
-  int staging;
   size_t ws_o_bytes;
+  size_t ws_lse_bytes;
 };
 
 int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* opts, bool paged,
-              Plan* out) {
+              bool query_device, Plan* out) {
   if (!opts || opts->struct_size < sizeof(gqa_decode_opts)) return GQA_ERR_INVALID_ARGUMENT;
   if (B <= 0 || H <= 0 || G <= 0 || d_h <= 0 || q_len <= 0) return GQA_ERR_INVALID_ARGUMENT;
   if (G > H || H % G != 0) return GQA_ERR_INVALID_ARGUMENT;
@@ -42,7 +67,6 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
   if (opts->causal != 0 && opts->causal != 1) return GQA_ERR_INVALID_ARGUMENT;
   if (opts->num_splits < 0 || opts->chunk_tokens < 0) return GQA_ERR_INVALID_ARGUMENT;
   if (opts->policy < GQA_POLICY_AUTO || opts->policy > GQA_POLICY_MFMA) return GQA_ERR_INVALID_ARGUMENT;
-  if (opts->staging < 0 || opts->staging > 2) return GQA_ERR_INVALID_ARGUMENT;
 
   const int hpg = H / G;
   const long long R = (long long)hpg * q_len;
@@ -71,19 +95,47 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
     policy = (opts->dtype == GQA_DTYPE_BF16 && R >= 4) ? GQA_POLICY_MFMA : GQA_POLICY_VALU;
   if (policy == GQA_POLICY_MFMA && opts->dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
 
-  int tile, row_block = 1, n_rb = 1, lds;
+  gqa_plan& pub = p.pub;
+  pub.policy = policy;
+  pub.rows = (int)R;
+  pub.capacity = capacity;
+  pub.block_threads = 256;
+
   if (policy == GQA_POLICY_MFMA) {
-    const int staging = opts->staging == 1 ? 0 : 1;  // default: register ring
-    const gqa::MfmaVariant v = gqa::mfma_variant_for_rows((int)R, d_h, staging);
-    p.staging = staging;
-    tile = v.tile;
-    lds = v.lds_bytes;
-  } else {
-    row_block = R >= 8 ? 8 : (R >= 4 ? 4 : (R >= 2 ? 2 : 1));
-    n_rb = (int)((R + row_block - 1) / row_block);
-    tile = gqa::valu_tile_tokens(opts->dtype, d_h);
-    lds = gqa::valu_lds_bytes(opts->dtype, d_h, row_block);
+    // Persistent balanced schedule: the (sequence, group) segments, cut into 32-key
+    // tiles and laid end to end, are shared equally by every workgroup the device
+    // holds at once; num_splits > 0 forces the workgroup count instead.
+    const long long max_tiles = (long long)B * G * ((capacity + kMfmaTile - 1) / kMfmaTile);
+    if (max_tiles > INT32_MAX / 2) return GQA_ERR_UNSUPPORTED;
+    const gqa::MfmaVariant v = gqa::mfma_variant_for_rows((int)R, d_h, paged, query_device);
+    int nwg = opts->num_splits;
+    if (nwg == 0) {
+      const int per_cu = v.wgs_per_cu > 0 ? v.wgs_per_cu : kDefaultWgsPerCu;
+      nwg = (query_device ? device_cus() : kDefaultCUs) * per_cu;
+    }
+    if (nwg > (1 << 20)) return GQA_ERR_UNSUPPORTED;
+    pub.schedule = 1;
+    pub.row_blocks = 1;
+    pub.tile_tokens = kMfmaTile;
+    pub.chunk_tokens = 0;
+    pub.max_splits = 2;
+    pub.workgroups = nwg;
+    pub.grid[0] = nwg;
+    pub.grid[1] = 1;
+    pub.grid[2] = 1;
+    pub.lds_bytes = v.lds_bytes;
+    const size_t prow = (size_t)nwg * 2 * (size_t)R;
+    p.ws_o_bytes = round_up(prow * d_h * sizeof(float), kWsAlign);
+    p.ws_lse_bytes = round_up(prow * sizeof(float), kWsAlign);
+    pub.workspace_bytes = p.ws_o_bytes + p.ws_lse_bytes + round_up(((size_t)B + 1) * sizeof(int32_t), kWsAlign);
+    *out = p;
+    return GQA_OK;
   }
+
+  // split-K grid over (split, group x row block, sequence): the VALU policy
+  const int row_block = R >= 8 ? 8 : (R >= 4 ? 4 : (R >= 2 ? 2 : 1));
+  const int n_rb = (int)((R + row_block - 1) / row_block);
+  const int tile = gqa::valu_tile_tokens(opts->dtype, d_h);
   if ((long long)G * n_rb > 65535) return GQA_ERR_UNSUPPORTED;
 
   const long long cap_tiles = ((long long)capacity + tile - 1) / tile * tile;
@@ -94,11 +146,10 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
     const long long per = ((long long)capacity + opts->num_splits - 1) / opts->num_splits;
     chunk = (per + tile - 1) / tile * tile;
   } else {
-    // Enough workgroup slots to balance ragged lengths over 256 CUs, but keep each
-    // split long enough that its fp32 partials (R rows) stay small next to its KV
-    // bytes and its pipeline prologue is amortised.
+    // Enough workgroup slots to balance ragged lengths, but each split long enough
+    // that its fp32 partials stay small next to its KV bytes.
     const long long units = (long long)B * G * n_rb;
-    long long par = (long long)capacity * units / kTargetSlots;
+    const long long par = (long long)capacity * units / kTargetSlots;
     long long lo = 4LL * tile;
     if (16 * R > lo) lo = 16 * R;
     chunk = par > lo ? par : lo;
@@ -109,27 +160,22 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
   const long long splits = ((long long)capacity + chunk - 1) / chunk;
   if (splits > INT32_MAX / 2) return GQA_ERR_UNSUPPORTED;
 
-  gqa_plan& pub = p.pub;
-  pub.policy = policy;
-  pub.rows = (int)R;
+  pub.schedule = 0;
   pub.row_blocks = n_rb;
   pub.tile_tokens = tile;
   pub.chunk_tokens = (int)chunk;
   pub.max_splits = (int)splits;
-  pub.capacity = capacity;
+  pub.workgroups = (int)(splits * G * n_rb * B > INT32_MAX ? INT32_MAX : splits * G * n_rb * B);
   pub.grid[0] = (int)splits;
   pub.grid[1] = G * n_rb;
   pub.grid[2] = B;
-  pub.block_threads = 256;
-  pub.lds_bytes = lds;
+  pub.lds_bytes = gqa::valu_lds_bytes(opts->dtype, d_h, row_block);
   p.row_block = row_block;
   if (splits > 1) {
     const size_t rows = (size_t)B * q_len * H * (size_t)splits;
     p.ws_o_bytes = round_up(rows * d_h * sizeof(float), kWsAlign);
-    pub.workspace_bytes = p.ws_o_bytes + round_up(rows * sizeof(float), kWsAlign);
-  } else {
-    p.ws_o_bytes = 0;
-    pub.workspace_bytes = 0;
+    p.ws_lse_bytes = round_up(rows * sizeof(float), kWsAlign);
+    pub.workspace_bytes = p.ws_o_bytes + p.ws_lse_bytes;
   }
   *out = p;
   return GQA_OK;
@@ -164,9 +210,12 @@ const char* gqa_status_string(int status) {
 int gqa_decode_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* opts,
                     gqa_plan* plan) {
   if (!plan || !opts) return GQA_ERR_INVALID_ARGUMENT;
-  Plan p;
   const bool paged = opts->struct_size >= sizeof(gqa_decode_opts) && opts->page_size > 0;
-  const int st = make_plan(B, H, G, d_h, q_len, opts, paged, &p);
+  Plan p;
+  int st = make_plan(B, H, G, d_h, q_len, opts, paged, /*query_device=*/false, &p);
+  if (st != GQA_OK) return st;
+  // arguments are valid: the device may now be asked how many workgroups it holds
+  st = make_plan(B, H, G, d_h, q_len, opts, paged, /*query_device=*/true, &p);
   if (st != GQA_OK) return st;
   *plan = p.pub;
   return GQA_OK;
@@ -190,12 +239,16 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const in
       !aligned(seq_lens, 4) || (block_table && !aligned(block_table, 4)))
     return GQA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+  if (opts->struct_size >= sizeof(gqa_decode_opts) && !block_table && opts->page_size != 0)
+    return GQA_ERR_INVALID_ARGUMENT;
+  const bool paged = block_table != nullptr;
   Plan p;
-  const int st = make_plan(B, H, G, d_h, q_len, opts, block_table != nullptr, &p);
+  int st = make_plan(B, H, G, d_h, q_len, opts, paged, /*query_device=*/false, &p);
   if (st != GQA_OK) return st;
-  if (!block_table && opts->page_size != 0) return GQA_ERR_INVALID_ARGUMENT;
+  st = make_plan(B, H, G, d_h, q_len, opts, paged, /*query_device=*/true, &p);
+  if (st != GQA_OK) return st;
   const gqa_plan& pl = p.pub;
-  if (pl.max_splits > 1) {
+  if (pl.workspace_bytes > 0) {
     if (!opts->workspace || !aligned(opts->workspace, kWsAlign) ||
         opts->workspace_bytes < pl.workspace_bytes)
       return GQA_ERR_WORKSPACE;
@@ -208,9 +261,11 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const in
   dp.seq_lens = seq_lens;
   dp.table = block_table;
   dp.out = out;
-  if (pl.max_splits > 1) {
-    dp.ws_o = static_cast<float*>(opts->workspace);
-    dp.ws_lse = reinterpret_cast<float*>(static_cast<unsigned char*>(opts->workspace) + p.ws_o_bytes);
+  if (pl.workspace_bytes > 0) {
+    unsigned char* ws = static_cast<unsigned char*>(opts->workspace);
+    dp.ws_o = reinterpret_cast<float*>(ws);
+    dp.ws_lse = reinterpret_cast<float*>(ws + p.ws_o_bytes);
+    dp.ws_prefix = reinterpret_cast<int32_t*>(ws + p.ws_o_bytes + p.ws_lse_bytes);
   }
   dp.B = B;
   dp.H = H;
@@ -227,7 +282,7 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const in
   dp.causal = opts->causal;
   dp.row_block = p.row_block;
   dp.n_row_blocks = pl.row_blocks;
-  dp.staging = p.staging;
+  dp.nwg = pl.workgroups;
   dp.qk_scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -239,7 +294,10 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const in
                      : gqa::launch_decode_valu(dp, opts->dtype, d_h, p.paged, grid, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
   if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return GQA_ERR_HIP;
-  if (pl.max_splits > 1) {
+  if (pl.policy == GQA_POLICY_MFMA) {
+    e = gqa::launch_merge_persistent(dp, d_h, s);
+    if (e != hipSuccess) return GQA_ERR_HIP;
+  } else if (pl.max_splits > 1) {
     e = gqa::launch_merge(dp, opts->dtype, d_h, s);
     if (e != hipSuccess) return GQA_ERR_HIP;
   }

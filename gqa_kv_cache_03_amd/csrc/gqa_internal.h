@@ -6,7 +6,7 @@
 
 namespace gqa {
 
-// Everything a split-K decode kernel needs; passed by value as the kernel argument.
+// Everything a decode kernel needs; passed by value as the kernel argument.
 struct DecodeParams {
   const void* q;           // [B, q_len, H, D]
   const void* k;           // contiguous [B, G, cap, D] or paged [pages, G, P, D]
@@ -14,8 +14,12 @@ struct DecodeParams {
   const int32_t* seq_lens; // [B]
   const int32_t* table;    // [B, max_blocks] or nullptr
   void* out;               // [B, q_len, H, D]
-  float* ws_o;             // [B, q_len, H, max_splits, D] fp32 (split partials, normalised)
-  float* ws_lse;           // [B, q_len, H, max_splits] fp32, log2-domain log-sum-exp
+  // split partials (normalised O, log2-domain log-sum-exp):
+  //   split-K grid (VALU): ws_o [B, q_len, H, max_splits, D], ws_lse [B, q_len, H, max_splits]
+  //   persistent (MFMA):   ws_o [nwg, 2, R, D], ws_lse [nwg, 2, R], ws_prefix [B + 1]
+  float* ws_o;
+  float* ws_lse;
+  int32_t* ws_prefix;      // tiles before sequence b's segments (persistent schedule)
   int B, H, G, q_len;
   int hpg;                 // H / G
   int R;                   // hpg * q_len packed rows per group
@@ -28,7 +32,7 @@ struct DecodeParams {
   int causal;
   int row_block;           // rows per workgroup along grid.y (VALU policy)
   int n_row_blocks;
-  int staging;             // MFMA kernel: 0 LDS-DMA ring, 1 register ring
+  int nwg;                 // persistent workgroups (MFMA policy)
   float qk_scale_log2;     // scale * log2(e): logits in base-2 units
 };
 
@@ -40,14 +44,16 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int d_h, bool pa
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int d_h, bool paged,
                               dim3 grid, hipStream_t stream);
 hipError_t launch_merge(const DecodeParams& p, int dtype, int d_h, hipStream_t stream);
+hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t stream);
 
-// Static geometry of the MFMA kernel variants, chosen by packed row count R.
+// Geometry of the MFMA kernel variants, chosen by packed row count R.
 struct MfmaVariant {
-  int max_rows;    // R this variant serves (multiple of 16)
-  int tile;        // keys per pipeline step
-  int lds_bytes;   // dynamic LDS per workgroup (D = 128)
+  int max_rows;      // R this variant serves (multiple of 16)
+  int tile;          // keys per pipeline step
+  int lds_bytes;     // LDS per workgroup
+  int wgs_per_cu;    // resident workgroups per CU (0 when not queried / no device)
 };
-MfmaVariant mfma_variant_for_rows(int R, int d_h, int staging);
+MfmaVariant mfma_variant_for_rows(int R, int d_h, bool paged, bool query_device);
 int valu_tile_tokens(int dtype, int d_h);
 int valu_lds_bytes(int dtype, int d_h, int row_block);
 

@@ -9,9 +9,20 @@
 // Formulation", evaluated piecewise). Splits past the sequence end were never
 // written and are not read; empty splits carry lse = -inf and weigh nothing.
 //
-// One 256-thread workgroup per output row (b, t, h). A split's D partial values are
-// read by D/4 lanes with 16-byte loads; the workgroup walks 4 * (256 / D) splits per
-// round, several rounds in flight per lane, and reduces across waves through LDS.
+// Split-K grid: one 256-thread workgroup per output row (b, t, h). A split's D
+// partial values are read by D/4 lanes with 16-byte loads; the workgroup walks
+// 4 * (256 / D) splits per round, several rounds in flight per lane, and reduces
+// across waves through LDS.
+//
+// Persistent schedule: the decode kernel's workgroups share one flat sequence of
+// key tiles (segment (b, g) = the n_b tiles of sequence b and KV group g, segments
+// in (b, g) order). Workgroup w owns tiles [lo(w), hi(w)), lo(w) = floor(w W / nwg).
+// A segment inside one workgroup was written straight to the output; a segment cut
+// by workgroup boundaries left one partial per workgroup it touches: in the
+// workgroup's slot 0 if the segment holds the workgroup's first tile, else in
+// slot 1 (it is then that workgroup's last segment). The merge recomputes the same
+// ownership from the prefix sums the decode kernel published. One workgroup per
+// (segment, packed row).
 
 #include "gqa_internal.h"
 
@@ -115,7 +126,117 @@ hipError_t go(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+constexpr int kPersistSlots = 2;
+
+__device__ __forceinline__ int tile_lo(int w, int W, int nwg) {
+  return (int)(((long long)w * W) / nwg);
+}
+
+// Workgroup owning flat tile f: the largest w with lo(w) <= f.
+__device__ __forceinline__ int tile_owner(int f, int W, int nwg) {
+  return (int)((((long long)f + 1) * nwg - 1) / W);
+}
+
+// One workgroup per (segment, row): D/4 lanes cover the row's D columns and the
+// workgroup's 256 / (D/4) lane groups take the segment's partials in turn, several
+// in flight per lane, each group keeping a running max; the groups then combine
+// through LDS.
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams p) {
+  constexpr int LPR = D / 4;               // lanes per row (4 columns each)
+  constexpr int NGRP = kThreads / LPR;     // partial groups
+  constexpr int U = 4;                     // partials in flight per lane
+  __shared__ float sm_m[NGRP];
+  __shared__ float sm_l[NGRP];
+  __shared__ f32x4 sm_o[NGRP][LPR];
+
+  const int seg = blockIdx.x / p.R;
+  const int r = blockIdx.x - seg * p.R;
+  const int b = seg / p.G;
+  const int g = seg - b * p.G;
+  const int W = p.ws_prefix[p.B];
+  const int pre = p.ws_prefix[b];
+  const int n = (p.ws_prefix[b + 1] - pre) / p.G;  // tiles per segment of b
+  if (n <= 0 || W <= 0) return;
+  const int s0 = pre + g * n;
+  const int wa = tile_owner(s0, W, p.nwg);
+  const int wb = tile_owner(s0 + n - 1, W, p.nwg);
+  if (wa == wb) return;  // written whole by one workgroup
+
+  const int tid = threadIdx.x;
+  const int grp = tid / LPR;
+  const int c = (tid % LPR) * 4;
+  const int slot_a = tile_lo(wa, W, p.nwg) < s0 ? 1 : 0;
+
+  float m = kNegInf, l = 0.f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int base = wa + grp; base <= wb; base += NGRP * U) {
+    float lse[U];
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = base + u * NGRP;
+      lse[u] = kNegInf;
+      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (w <= wb && tile_lo(w, W, p.nwg) < tile_lo(w + 1, W, p.nwg)) {  // else empty
+        const size_t prow = ((size_t)w * kPersistSlots + (w == wa ? slot_a : 0)) * p.R + r;
+        lse[u] = p.ws_lse[prow];
+        v[u] = *reinterpret_cast<const f32x4*>(p.ws_o + prow * D + c);
+      }
+    }
+    float mu = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mu = fmaxf(mu, lse[u]);
+    if (mu == kNegInf) continue;  // nothing visible yet
+    const float sc = __builtin_amdgcn_exp2f(m - mu);  // 0 while m = -inf
+    acc *= sc;
+    l *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wt = __builtin_amdgcn_exp2f(lse[u] - mu);
+      acc += wt * v[u];
+      l += wt;
+    }
+    m = mu;
+  }
+  if (tid % LPR == 0) {
+    sm_m[grp] = m;
+    sm_l[grp] = l;
+  }
+  sm_o[grp][tid % LPR] = acc;
+  __syncthreads();
+  if (grp != 0) return;
+  float M = kNegInf;
+#pragma unroll
+  for (int k = 0; k < NGRP; ++k) M = fmaxf(M, sm_m[k]);
+  const float Mu = (M == kNegInf) ? 0.f : M;
+  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lt = 0.f;
+#pragma unroll
+  for (int k = 0; k < NGRP; ++k) {
+    const float wt = __builtin_amdgcn_exp2f(sm_m[k] - Mu);
+    tot += wt * sm_o[k][tid];
+    lt += wt * sm_l[k];
+  }
+  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+  const int t = r / p.hpg;
+  const int h = g * p.hpg + (r - t * p.hpg);
+  const size_t orow = ((size_t)b * p.q_len + t) * p.H + h;
+  put4<__bf16>(static_cast<__bf16*>(p.out) + orow * D + c, tot * inv);
+}
+
+template <int D>
+hipError_t go_persistent(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid(p.B * p.G * p.R);
+  hipLaunchKernelGGL((merge_persistent_kernel<D>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t stream) {
+  return d_h == 64 ? go_persistent<64>(p, stream) : go_persistent<128>(p, stream);
+}
 
 hipError_t launch_merge(const DecodeParams& p, int dtype, int d_h, hipStream_t stream) {
   if (dtype == 0) return d_h == 64 ? go<float, 64>(p, stream) : go<float, 128>(p, stream);

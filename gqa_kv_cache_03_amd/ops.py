@@ -13,7 +13,6 @@ from . import _lib
 from ._lib import DecodeOpts, GqaError, Plan
 
 _POLICIES = {"auto": _lib.GQA_POLICY_AUTO, "valu": _lib.GQA_POLICY_VALU, "mfma": _lib.GQA_POLICY_MFMA}
-_STAGING = {"auto": 0, "dma": 1, "regs": 2}
 
 
 def _dtype_code(torch, dt) -> int:
@@ -26,7 +25,7 @@ def _dtype_code(torch, dt) -> int:
 
 def make_opts(*, dtype_code: int, causal: bool, capacity: int, page_size: int = 0,
               max_blocks: int = 0, num_pages: int = 0, num_splits: int = 0,
-              chunk_tokens: int = 0, policy: str = "auto", staging: str = "auto") -> DecodeOpts:
+              chunk_tokens: int = 0, policy: str = "auto") -> DecodeOpts:
     o = _lib.default_opts()
     o.dtype = dtype_code
     o.causal = 1 if causal else 0
@@ -37,7 +36,6 @@ def make_opts(*, dtype_code: int, causal: bool, capacity: int, page_size: int = 
     o.num_splits = num_splits
     o.chunk_tokens = chunk_tokens
     o.policy = _POLICIES[policy]
-    o.staging = _STAGING[staging]
     return o
 
 
@@ -58,12 +56,12 @@ def _geometry(q, k_cache, block_table):
 
 
 def plan(q, k_cache, block_table=None, *, causal=True, num_splits=0, chunk_tokens=0,
-         policy="auto", staging="auto") -> dict:
+         policy="auto") -> dict:
     """What gqa_decode would launch for these tensors (no device work)."""
     import torch
     B, q_len, H, d, G, geo = _geometry(q, k_cache, block_table)
     o = make_opts(dtype_code=_dtype_code(torch, q.dtype), causal=causal, num_splits=num_splits,
-                  chunk_tokens=chunk_tokens, policy=policy, staging=staging, **geo)
+                  chunk_tokens=chunk_tokens, policy=policy, **geo)
     pl = Plan()
     st = _lib.lib().gqa_decode_plan(B, H, G, d, q_len, ctypes.byref(o), ctypes.byref(pl))
     if st != _lib.GQA_OK:
@@ -73,12 +71,14 @@ def plan(q, k_cache, block_table=None, *, causal=True, num_splits=0, chunk_token
 
 def gqa_decode(q, k_cache, v_cache, seq_lens, block_table=None, *, scale: Optional[float] = None,
                out=None, causal: bool = True, num_splits: int = 0, chunk_tokens: int = 0,
-               policy: str = "auto", staging: str = "auto", workspace=None, profile_events=None):
+               policy: str = "auto", workspace=None, profile_events=None):
     """One GQA decode step on the current HIP stream; returns `out`.
 
     q [B, q_len, H, d_h]; k_cache/v_cache [B, G, cap, d_h] (contiguous) or
     [num_pages, G, page_size, d_h] with block_table int32 [B, max_blocks];
     seq_lens int32 [B] counting the q_len new tokens. scale defaults to 1/sqrt(d_h).
+    num_splits: MFMA policy -- persistent workgroups (0: what the device holds);
+    VALU policy -- maximum context splits per sequence (0: heuristic).
     """
     import torch
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
@@ -102,7 +102,7 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, block_table=None, *, scale: Option
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = make_opts(dtype_code=code, causal=causal, num_splits=num_splits, chunk_tokens=chunk_tokens,
-                  policy=policy, staging=staging, **geo)
+                  policy=policy, **geo)
     L = _lib.lib()
     need = ctypes.c_size_t(0)
     st = L.gqa_decode_workspace_size(B, H, G, d, q_len, ctypes.byref(o), ctypes.byref(need))

@@ -62,34 +62,39 @@ typedef struct gqa_decode_opts {
   int32_t  page_size;         /* paged: tokens per page, a power of two in [16, 256] */
   int32_t  max_blocks_per_seq;/* paged: row stride of block_table */
   int32_t  num_pages;         /* paged: pages in the pool (entries are clamped to it) */
-  int32_t  num_splits;        /* 0: library heuristic; n > 0: at most n context splits */
-  int32_t  chunk_tokens;      /* 0: from num_splits/heuristic; else tokens per split
+  int32_t  num_splits;        /* 0: library choice. MFMA policy: number of persistent
+                                 workgroups sharing the work; VALU policy: at most this
+                                 many context splits per sequence */
+  int32_t  chunk_tokens;      /* VALU policy only: 0 or tokens per context split
                                  (rounded up to the kernel's tile) */
   int32_t  policy;            /* gqa_policy */
-  int32_t  staging;           /* MFMA policy's K/V staging: 0 library choice, 1 direct
-                                 global->LDS ring, 2 register prefetch ring */
-  void*    workspace;         /* device scratch for split-K partials (caller-owned) */
+  void*    workspace;         /* device scratch for split partials (caller-owned) */
   size_t   workspace_bytes;
   void*    profile_events[3]; /* optional hipEvent_t: recorded on `stream` before the
-                                 split kernel, between it and the merge, after the merge */
+                                 decode kernel, between it and the merge, after the merge */
 } gqa_decode_opts;
 
-/* What the library will launch for a shape (host-only, no HIP call). */
+/* What the library will launch for a shape (no device work; with a GPU present the
+ * persistent schedule's workgroup count comes from the device). */
 typedef struct gqa_plan {
   int32_t policy;             /* GQA_POLICY_VALU or GQA_POLICY_MFMA */
+  int32_t schedule;           /* 0: split-K grid (splits, G*row_blocks, B);
+                                 1: persistent balanced workgroups (grid[0] of them) */
   int32_t rows;               /* R = (H/G) * q_len query rows per KV group */
   int32_t row_blocks;         /* workgroups that share one (b, g, split) along rows */
   int32_t tile_tokens;        /* keys staged per pipeline step */
-  int32_t chunk_tokens;       /* keys per context split */
-  int32_t max_splits;         /* ceil(capacity / chunk_tokens) */
+  int32_t chunk_tokens;       /* split-K grid: keys per context split; else 0 */
+  int32_t max_splits;         /* split-K grid: ceil(capacity / chunk_tokens);
+                                 persistent: partial slots per workgroup (2) */
+  int32_t workgroups;         /* workgroups launched by the decode kernel */
   int32_t capacity;           /* tokens addressable per sequence */
-  int32_t grid[3];            /* split kernel grid (splits, G*row_blocks, B) */
+  int32_t grid[3];            /* decode kernel grid */
   int32_t block_threads;
   int32_t lds_bytes;
-  size_t  workspace_bytes;    /* 0 when max_splits == 1 (the split kernel writes out) */
+  size_t  workspace_bytes;    /* 0 when no partial results are needed */
 } gqa_plan;
 
-/* Fill *opts with defaults: struct_size set, bf16, causal, heuristic splits, AUTO. */
+/* Fill *opts with defaults: struct_size set, bf16, causal, library-chosen splits, AUTO. */
 void gqa_decode_opts_init(gqa_decode_opts* opts);
 
 /*
@@ -117,9 +122,10 @@ void gqa_decode_opts_init(gqa_decode_opts* opts);
  *
  * Errors: INVALID_ARGUMENT for NULL or misaligned pointers, non-positive sizes,
  * H % G != 0, non-finite scale, a bad opts struct or paged geometry; UNSUPPORTED for
- * d_h not in {64,128}, an unknown dtype, R = (H/G)*q_len > 256 or a forced MFMA
- * policy with fp32; WORKSPACE when more than one split is planned and workspace is
- * NULL, too small or not 256-byte aligned; HIP when a launch fails.
+ * d_h not in {64,128}, an unknown dtype, R = (H/G)*q_len > 256, a forced MFMA
+ * policy with fp32 or sizes whose tile counts overflow int32; WORKSPACE when the
+ * plan needs workspace (gqa_decode_workspace_size) and it is NULL, too small or not
+ * 256-byte aligned; HIP when a launch or event record fails.
  */
 int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                const int32_t* seq_lens, const int32_t* block_table, void* out,

@@ -115,7 +115,6 @@ def test_opts_checks():
     assert call(q_len=4, o=opts(cache_capacity=3)) == INV
     assert call(o=opts(num_splits=-1)) == INV
     assert call(o=opts(policy=9)) == INV
-    assert call(o=opts(staging=3)) == INV
     assert call(o=opts(dtype=_lib.GQA_DTYPE_F32, policy=_lib.GQA_POLICY_MFMA)) == UNS
     assert call(o=opts(page_size=16)) == INV           # page size without a block table
 
@@ -130,16 +129,19 @@ def test_paged_geometry_checks():
 
 
 def test_workspace_required_when_split():
-    o = opts(num_splits=4)
-    assert call(o=o) == WS
-    st, pl = plan(o=o)
-    assert st == OK and pl.max_splits == 4 and pl.workspace_bytes > 0
-    o.workspace = 1000                                   # misaligned
-    o.workspace_bytes = pl.workspace_bytes
-    assert call(o=o) == WS
-    o.workspace = 4096
-    o.workspace_bytes = pl.workspace_bytes - 1
-    assert call(o=o) == WS
+    for o in (opts(num_splits=4, policy=_lib.GQA_POLICY_VALU), opts(num_splits=7)):
+        assert call(o=o) == WS
+        st, pl = plan(o=o)
+        assert st == OK and pl.workspace_bytes > 0
+        o.workspace = 1000                                   # misaligned
+        o.workspace_bytes = pl.workspace_bytes
+        assert call(o=o) == WS
+        o.workspace = 4096
+        o.workspace_bytes = pl.workspace_bytes - 1
+        assert call(o=o) == WS
+
+
+ro = lambda x: -(-x // 256) * 256
 
 
 def test_plan_policy_and_workspace_formula():
@@ -149,19 +151,37 @@ def test_plan_policy_and_workspace_formula():
     assert pl.policy == _lib.GQA_POLICY_VALU and pl.rows == 1
     st, pl = plan(H=8, G=2, o=opts(dtype=_lib.GQA_DTYPE_F32))
     assert pl.policy == _lib.GQA_POLICY_VALU
-    # forced splits: chunk is ceil(cap / n) rounded up to the tile
-    st, pl = plan(B=3, H=16, G=4, q_len=2, o=opts(cache_capacity=1000, num_splits=3))
-    assert st == OK
+    # split-K grid (VALU): chunk is ceil(cap / n) rounded up to the tile
+    st, pl = plan(B=3, H=16, G=4, q_len=2, o=opts(cache_capacity=1000, num_splits=3,
+                                                  policy=_lib.GQA_POLICY_VALU))
+    assert st == OK and pl.schedule == 0
     assert pl.chunk_tokens % pl.tile_tokens == 0
     assert pl.chunk_tokens >= -(-1000 // 3)
     assert pl.max_splits == -(-1000 // pl.chunk_tokens) <= 3
     rows = 3 * 2 * 16 * pl.max_splits
-    ro = lambda x: -(-x // 256) * 256
     assert pl.workspace_bytes == ro(rows * 128 * 4) + ro(rows * 4)
     assert list(pl.grid) == [pl.max_splits, 4, 3]
-    # single split needs no workspace
-    st, pl = plan(o=opts(num_splits=1))
+    st, pl = plan(o=opts(num_splits=1, policy=_lib.GQA_POLICY_VALU))   # one split: no workspace
     assert pl.max_splits == 1 and pl.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("nwg", [1, 5, 600])
+def test_persistent_plan_and_workspace_formula(nwg):
+    """MFMA policy: num_splits is the persistent workgroup count; each holds two
+    partial slots of R rows, plus B + 1 prefix sums."""
+    B, H, G, q_len, d = 3, 16, 4, 2, 128
+    st, pl = plan(B=B, H=H, G=G, q_len=q_len, d=d, o=opts(cache_capacity=1000, num_splits=nwg))
+    assert st == OK and pl.policy == _lib.GQA_POLICY_MFMA and pl.schedule == 1
+    R = H // G * q_len
+    assert pl.workgroups == nwg and list(pl.grid) == [nwg, 1, 1] and pl.max_splits == 2
+    assert pl.workspace_bytes == ro(nwg * 2 * R * d * 4) + ro(nwg * 2 * R * 4) + ro((B + 1) * 4)
+
+
+def test_persistent_default_fills_the_device():
+    """Without a device to query, the default is two workgroups on each of 256 CUs."""
+    st, pl = plan(H=32, G=8, o=opts(cache_capacity=4096))
+    assert st == OK and pl.schedule == 1
+    assert pl.workgroups == 512
 
 
 @pytest.mark.parametrize("R", [1, 2, 3, 4, 8, 16, 17, 32, 64, 65, 128, 256])

@@ -59,28 +59,28 @@ CASES = [
 
 
 @pytest.mark.parametrize("B,H,G,d,q_len,lens,dtype,page", CASES)
-@pytest.mark.parametrize("splits", [0, 1, 3])
-@pytest.mark.parametrize("staging", ["regs", "dma"])
-def test_matches_oracle(B, H, G, d, q_len, lens, dtype, page, splits, staging):
+@pytest.mark.parametrize("splits", [0, 1, 3, 37])
+def test_matches_oracle(B, H, G, d, q_len, lens, dtype, page, splits):
     wl, lens = small_workload(B, H, G, d, q_len, lens, dtype=dtype, paged=page,
                               seed=1000 + B * 7 + H + G + d + q_len + page)
     inp = make(wl, lens)
-    got = run(inp, num_splits=splits, staging=staging)
+    got = run(inp, num_splits=splits)
     ref = oracle_for(inp)
-    assert_parity(got, ref, dtype, f"{wl.name} splits={splits} staging={staging}")
+    assert_parity(got, ref, dtype, f"{wl.name} splits={splits}")
 
 
-@pytest.mark.parametrize("staging", ["regs", "dma"])
 @pytest.mark.parametrize("R_case", [(32, 8, 1, 4), (32, 4, 1, 4), (32, 2, 4, 2), (32, 1, 4, 2), (64, 1, 4, 2)])
-@pytest.mark.parametrize("chunk", [64, 192, 512, 4096])
-def test_pipeline_depths(staging, R_case, chunk):
-    """Splits from one tile to many: exercises the prologue, steady state and drain
-    of each staging pipeline (and the short-split path) for every wave layout."""
+@pytest.mark.parametrize("nwg", [1, 2, 5, 64, 333, 5000])
+def test_persistent_boundaries(R_case, nwg):
+    """Persistent workgroup counts from one (every segment inside one workgroup, many
+    segment switches) to more workgroups than tiles (empty workgroups, one-tile
+    shares): exercises the ring's prologue, steady state and drain, segment switches
+    and both partial slots for every wave layout."""
     H, G, q_len, B = R_case
     wl, lens = small_workload(B, H, G, 128, q_len, [3000, 97, 1, 650][:B], seed=77 + H + G)
     inp = make(wl, lens)
-    got = run(inp, chunk_tokens=chunk, staging=staging)
-    assert_parity(got, oracle_for(inp), "bfloat16", f"{staging} chunk={chunk} R={H // G * q_len}")
+    got = run(inp, num_splits=nwg, policy="mfma")
+    assert_parity(got, oracle_for(inp), "bfloat16", f"nwg={nwg} R={H // G * q_len}")
 
 
 @pytest.mark.parametrize("causal", [True, False])
