@@ -1,0 +1,79 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark
+times (the library's default plan, one call over the whole batch).
+
+Every output element must be finite: NaN fills every cache slot the step must not read.
+Sampled (sequence, KV group) units are compared element by element with the fp64
+oracle, which computes each unit on its own:
+
+- the first and the last unit;
+- a unit of the longest sequence;
+- a unit of the shortest sequence;
+- a seeded random one.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from gpu_cases import assert_parity, host64  # noqa: E402
+from gqa_synth import WORKLOADS, make_inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_kv_cache_03_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def sample_units(wl, lens):
+    rng = np.random.default_rng(wl.seed + 17)
+    b_long, b_short = int(np.argmax(lens)), int(np.argmin(lens))
+    units = [(0, 0), (wl.B - 1, wl.G - 1), (b_long, int(rng.integers(wl.G))),
+             (b_short, int(rng.integers(wl.G))), (int(rng.integers(wl.B)), int(rng.integers(wl.G)))]
+    return sorted(set(units))
+
+
+def oracle_unit(inp, b, g):
+    """fp64 oracle output [q_len, H/G, d_h] of one (sequence, KV group) unit."""
+    wl = inp.wl
+    hpg = wl.H // wl.G
+    L = int(inp.lens[b])
+    q = host64(inp.q[b:b + 1, :, g * hpg:(g + 1) * hpg])
+    if inp.block_table is None:
+        k = host64(inp.k_cache[b:b + 1, g:g + 1, :L])
+        v = host64(inp.v_cache[b:b + 1, g:g + 1, :L])
+    else:
+        P = wl.page_size
+        n = -(-L // P)
+        pages = torch.as_tensor(inp.table[b, :n].astype(np.int64), device=inp.k_cache.device)
+        k = host64(inp.k_cache[pages, g].reshape(n * P, wl.d_h)[:L])[None, None]
+        v = host64(inp.v_cache[pages, g].reshape(n * P, wl.d_h)[:L])[None, None]
+    return oracle.gqa_decode(q, k, v, inp.lens[b:b + 1], wl.scale, 1, causal=wl.causal)[0]
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_full_size_sampled_parity(name):
+    from gqa_kv_cache_03_amd import gqa_decode, plan
+    wl = WORKLOADS[name]
+    print(f"[fullsize] {name}: generating", flush=True)
+    inp = make_inputs(wl, device="cuda")
+    pl = plan(inp.q, inp.k_cache, inp.block_table, causal=wl.causal)
+    print(f"[fullsize] {name}: decode, plan {pl['policy']} / {pl['schedule']} / {pl['workgroups']} workgroups",
+          flush=True)
+    out = gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table,
+                     scale=wl.scale, causal=wl.causal)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all()), f"{name}: non-finite output"
+    hpg = wl.H // wl.G
+    for b, g in sample_units(wl, inp.lens):
+        ref = oracle_unit(inp, b, g)
+        got = host64(out[b, :, g * hpg:(g + 1) * hpg])
+        e = assert_parity(got, ref, wl.dtype, f"{name} unit (b={b}, g={g}, L={int(inp.lens[b])})")
+        print(f"[fullsize] {name} (b={b}, g={g}): max_abs {e['max_abs']:.2e} rel_l2 {e['rel_l2']:.2e}",
+              flush=True)
+    del inp, out
+    torch.cuda.empty_cache()
