@@ -42,6 +42,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -53,11 +54,19 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (factor 2^8)
 constexpr bf16x2 kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
+// Lanes l, l^16, l^32 and l^48 hold the same query row of an MFMA result. On gfx950
+// v_permlane32_swap(x, x) leaves {x[l], x[l^32]} in each lane and
+// v_permlane16_swap(x, x) leaves {x[l], x[l^16]} (checked with an in-bounds probe),
+// so two VALU swaps reduce across the four lanes without a trip through LDS.
 __device__ __forceinline__ float wave_max_across_groups(float x) {
-  // lanes l, l^16, l^32, l^48 hold the same query row
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+#else
   return x;
+#endif
 }
 
 __device__ __forceinline__ int wave_sum_i32(int x) {
@@ -78,9 +87,14 @@ __device__ __forceinline__ int wave_incl_scan_i32(int x) {
 }
 
 __device__ __forceinline__ float wave_sum_across_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
+#if defined(__HIP_DEVICE_COMPILE__)
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+#else
   return x;
+#endif
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding and all
@@ -313,6 +327,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     lim_min = p.causal ? (c.L - p.q_len) : (c.L - 1);
   };
 
+  // |scale| log2(e), kept away from 0 so that a masked -inf logit stays -inf; with a
+  // zero scale every visible exponent is then within 1e-20 of 0 and every weight
+  // rounds to exactly 1, as it should
+  const float qk_c = fmaxf(fabsf(p.qk_scale_log2), 1e-30f);
+  const unsigned q_sign = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;  // negative scale: flip q
+
   // packed query rows of segment (b, g), as B operands of S^T = K Q^T
   auto load_q = [&](const Cursor& c) {
 #pragma unroll
@@ -323,8 +343,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         const int h = c.g * p.hpg + (r - t * p.hpg);
         const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)(c.b * p.q_len + t) * p.H + h) * D;
 #pragma unroll
-        for (int cc = 0; cc < CC; ++cc)
-          qf[rt][cc] = *reinterpret_cast<const bf16x8*>(qrow + cc * 32 + g4 * 8);
+        for (int cc = 0; cc < CC; ++cc) {
+          const u32x4 bits = *reinterpret_cast<const u32x4*>(qrow + cc * 32 + g4 * 8) ^ q_sign;
+          qf[rt][cc] = __builtin_bit_cast(bf16x8, bits);
+        }
       } else {
 #pragma unroll
         for (int cc = 0; cc < CC; ++cc) qf[rt][cc] = bf16x8{};
@@ -333,7 +355,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   };
 
   // ---- 4. consume one staged tile: S^T = K Q^T, online softmax, O^T += V^T P^T ----
-  auto consume = [&](const unsigned char* ks, const unsigned char* vs, const int tile0) {
+  // masked: some key of the tile lies past a row's last visible key (only the last
+  // tile or two of a segment), so those logits are set to -inf first.
+  auto consume = [&](const unsigned char* ks, const unsigned char* vs, const int tile0, const bool masked) {
     f32x4 s[RTW][KB];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
@@ -353,31 +377,33 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       }
     }
 
-    // Online softmax (base 2). A row's reference max m only moves when a tile max
-    // exceeds it by more than 2^kRescaleLog2; until then exp2(x - m) <= 2^kRescaleLog2
-    // and O and l keep their scale, so most tiles skip the rescale (numerator and
-    // denominator share m, so the result is unchanged). P is rounded to bf16 for the
-    // PV product and the denominator sums those rounded weights (dot2 with (1, 1)),
-    // so the normalised weights sum to one.
-    const bool need_mask = (tile0 + T - 1) > lim_min;
+    // Online softmax (base 2). Logits are s * c with c = |scale| log2(e) > 0 (a
+    // negative scale was moved into the query's sign), so the row max is taken on the
+    // raw products and p = exp2(fma(s, c, -m)) costs one FMA per score. A row's
+    // reference max m only moves when a tile max exceeds it by more than
+    // 2^kRescaleLog2; until then p <= 2^kRescaleLog2 and O and l keep their scale, so
+    // most tiles skip the rescale (numerator and denominator share m). P is rounded to
+    // bf16 for the PV product and the denominator sums those rounded weights (dot2
+    // with (1, 1)), so the normalised weights sum to one.
     bf16x2 pk[RTW][KB][2];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-      float x[KB][4];
+      if (masked) {
+        // a real (uniform) branch: without the empty volatile statement the compiler
+        // turns the block into a compare and select per score on every tile
+        asm volatile("");
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (tile0 + kb * 16 + g4 * 4 + i > lim[rt]) s[rt][kb][i] = kNegInf;
+      }
       float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = s[rt][kb][i] * p.qk_scale_log2;
-          if (need_mask) {
-            const int j = tile0 + kb * 16 + g4 * 4 + i;
-            v = (j <= lim[rt]) ? v : kNegInf;
-          }
-          x[kb][i] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = wave_max_across_groups(mx);
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rt][kb][i]);
+      mx = wave_max_across_groups(mx) * qk_c;
       const bool grow = mx > m_run[rt] + kRescaleLog2;  // -inf + c = -inf: a first finite max grows
       if (__builtin_amdgcn_ballot_w64(grow)) {
         const float m_new = grow ? mx : m_run[rt];
@@ -387,14 +413,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         for (int cb = 0; cb < CBW; ++cb) o[rt][cb] *= alpha;
         m_run[rt] = m_new;
       }
-      const float m_use = (m_run[rt] == kNegInf) ? 0.f : m_run[rt];
+      const float neg_m = (m_run[rt] == kNegInf) ? 0.f : -m_run[rt];
       float sum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const bf16x2 e = {(__bf16)__builtin_amdgcn_exp2f(x[kb][2 * h] - m_use),
-                            (__bf16)__builtin_amdgcn_exp2f(x[kb][2 * h + 1] - m_use)};
+          const bf16x2 e = {(__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][kb][2 * h], qk_c, neg_m)),
+                            (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][kb][2 * h + 1], qk_c, neg_m))};
           pk[rt][kb][h] = e;
           sum = __builtin_amdgcn_fdot2_f32_bf16(e, kOnes2, sum, false);
         }
@@ -509,7 +535,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       advance(issue);
     }
     const unsigned char* ks = smem + (f % NS) * C::STAGE_BYTES;
-    consume(ks, ks + C::TENSOR_BYTES, cons.t * T);
+    const int tile0 = cons.t * T;
+    consume(ks, ks + C::TENSOR_BYTES, tile0, tile0 + T - 1 > lim_min);
     const bool seg_end = cons.t == cons.n - 1;
     if (seg_end || f == count - 1) {
       const bool complete = seg_from_start && seg_end;
