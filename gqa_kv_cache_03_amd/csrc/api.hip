@@ -22,7 +22,7 @@ constexpr int kTargetSlots = 8192;   // split-kernel workgroup slots the VALU he
 constexpr size_t kWsAlign = 256;
 constexpr int kMfmaTile = 32;        // keys per tile of the persistent MFMA schedule
 constexpr int kDefaultCUs = 256;     // MI355X, used when no device can be queried
-constexpr int kDefaultWgsPerCu = 2;
+constexpr int kWgsPerCu = 2;         // persistent workgroups per CU (fewer if fewer fit)
 constexpr int kMaxDevices = 64;
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -110,7 +110,9 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
     const gqa::MfmaVariant v = gqa::mfma_variant_for_rows((int)R, d_h, paged, query_device);
     int nwg = opts->num_splits;
     if (nwg == 0) {
-      const int per_cu = v.wgs_per_cu > 0 ? v.wgs_per_cu : kDefaultWgsPerCu;
+      // two per CU measured fastest; fewer when the variant's registers or LDS allow
+      // only one
+      const int per_cu = (v.wgs_per_cu > 0 && v.wgs_per_cu < kWgsPerCu) ? v.wgs_per_cu : kWgsPerCu;
       nwg = (query_device ? device_cus() : kDefaultCUs) * per_cu;
     }
     if (nwg > (1 << 20)) return GQA_ERR_UNSUPPORTED;

@@ -43,12 +43,18 @@ typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int kThreads = 256;
 constexpr int kTile = 32;        // keys per pipeline stage
-constexpr int kStages = 4;       // LDS ring depth
+// LDS ring depth and the number of tiles issued ahead of the one being consumed
+// (< kStages). Measured on MI355X with two workgroups per CU: one tile ahead (32 KiB
+// of K/V in flight per CU) streams faster than two or three, on every workload
+// shape here, so the ring is a double buffer.
+constexpr int kStages = 2;
+constexpr int kAhead = 1;
 [[maybe_unused]] constexpr int kNontemporal = 2;  // cache-policy bit for streaming loads
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleLog2 = 8.f;  // lazy-rescale threshold (factor 2^8)
@@ -111,6 +117,18 @@ __device__ __forceinline__ void wait_vm_and_sync() {
   asm volatile("" ::: "memory");
 }
 
+// Wait for the oldest staged tile when `after` later tiles (at most K) may stay in
+// flight, each LD loads per wave.
+template <int LD, int K>
+__device__ __forceinline__ void wait_tiles(int after) {
+  if constexpr (K == 0) {
+    wait_vm_and_sync<0>();
+  } else {
+    if (after >= K) wait_vm_and_sync<K * LD>();
+    else wait_tiles<LD, K - 1>(after);
+  }
+}
+
 // LDS swizzles (16-byte chunk index XOR a function of the row) so that the QK
 // A-operand reads (16 consecutive key rows, one chunk each) and the transposed V
 // reads (16 consecutive key rows, the same two chunks each) spread over the banks.
@@ -131,17 +149,69 @@ __device__ __forceinline__ void load16_to_lds(const unsigned char* src, unsigned
 #endif
 }
 
-// Transposed 64-bit LDS read (ds_read_b64_tr_b16). Within each 16-lane group, lane i
-// receives as element e the 16-bit element i % 4 of the 8 bytes addressed by lane
+// Transposed 64-bit LDS reads (ds_read_b64_tr_b16). Within each 16-lane group, lane
+// i receives as element e the 16-bit element i % 4 of the 8 bytes addressed by lane
 // 4e + i / 4 of the group (measured on gfx950 with an in-bounds probe).
-__device__ __forceinline__ bf16x4 lds_read_tr16(const unsigned char* p) {
+//
+// They are issued from asm blocks that also wait for their own results, so every
+// output register holds its data when the block ends. Issued through the builtin
+// instead, the compiler cannot rule out that the read aliases a direct-to-LDS load
+// still in flight and drains all of them (vmcnt(0)) before it, which leaves only the
+// tile being consumed in flight. The ring's own wait and barrier already order these
+// reads after the loads of the tile they read.
+//
+// One column block: rows r (address a) and r + 16 (a + HI) of the same columns.
+template <int HI>
+__device__ __forceinline__ void lds_read_tr16_x2(unsigned a, bf16x4& lo, bf16x4& hi) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p);
-  return __builtin_bit_cast(bf16x4, v);
+  u32x2 x, y;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:%3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x), "=&v"(y)
+      : "v"(a), "i"(HI)
+      : "memory");
+  lo = __builtin_bit_cast(bf16x4, x);
+  hi = __builtin_bit_cast(bf16x4, y);
 #else
-  (void)p;
-  return bf16x4{};
+  (void)a;
+  lo = hi = bf16x4{};
+#endif
+}
+
+// Two column blocks at addresses a and b.
+template <int HI>
+__device__ __forceinline__ void lds_read_tr16_x4(unsigned a, unsigned b, bf16x4& lo0, bf16x4& hi0,
+                                                 bf16x4& lo1, bf16x4& hi1) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  u32x2 x0, y0, x1, y1;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %5\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%6\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(y0), "=&v"(x1), "=&v"(y1)
+      : "v"(a), "v"(b), "i"(HI)
+      : "memory");
+  lo0 = __builtin_bit_cast(bf16x4, x0);
+  hi0 = __builtin_bit_cast(bf16x4, y0);
+  lo1 = __builtin_bit_cast(bf16x4, x1);
+  hi1 = __builtin_bit_cast(bf16x4, y1);
+#else
+  (void)a;
+  (void)b;
+  lo0 = hi0 = lo1 = hi1 = bf16x4{};
+#endif
+}
+
+// 32-bit LDS address of a pointer into __shared__ memory.
+__device__ __forceinline__ unsigned lds_addr(const unsigned char* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return (unsigned)(uintptr_t)(LDS_AS const unsigned char*)p;
+#else
+  return (unsigned)(uintptr_t)p;
 #endif
 }
 
@@ -164,6 +234,8 @@ template <int D, int NRW, int NCW, int RTW>
 struct MfmaCfg {
   static constexpr int T = kTile;
   static constexpr int NS = kStages;
+  static constexpr int AHEAD = kAhead;
+  static_assert(AHEAD >= 1 && AHEAD < NS, "a tile is refilled only after every wave has consumed it");
   static constexpr int KB = T / 16;           // 16-key blocks per tile
   static constexpr int CC = D / 32;           // k-steps of QK^T
   static constexpr int CB = D / 16;           // 16-column output blocks
@@ -190,7 +262,7 @@ struct Cursor {
 template <int D, int NRW, int NCW, int RTW, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   using C = MfmaCfg<D, NRW, NCW, RTW>;
-  constexpr int T = C::T, NS = C::NS, KB = C::KB, CC = C::CC, CBW = C::CBW;
+  constexpr int T = C::T, NS = C::NS, AHEAD = C::AHEAD, KB = C::KB, CC = C::CC, CBW = C::CBW;
   constexpr int CPR = C::CPR, LOADS = C::LOADS, LD = C::LD, ROW_BYTES = C::ROW_BYTES;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
 
@@ -431,10 +503,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     // 4 * g4 + e of block 0 (e < 4), then of block 1 (e >= 4); a V^T fragment (4 keys of
     // one column per lane) is one transposed LDS read: lane p of a 16-lane group points
     // at key row base + p / 4, columns c0 + 4 (p % 4) .. +3.
-    auto vt4 = [&](int key_base, int c0) -> bf16x4 {
-      const int r = key_base + (l16 >> 2);
+    // LDS address of this lane's V^T fragment for column block cb (rows g4 * 4 ..;
+    // the second half of the k-slots is the same columns 16 rows further on, with the
+    // same swizzle)
+    auto vt_addr = [&](int cb) -> unsigned {
+      const int c0 = (cw * CBW + cb) * 16;
+      const int r = g4 * 4 + (l16 >> 2);
       const int c = c0 + ((l16 & 3) << 2);
-      return lds_read_tr16(vs + r * ROW_BYTES + ((((c >> 3) ^ swz_v<CPR>(r)) << 4) | ((c & 7) << 1)));
+      return lds_addr(vs + r * ROW_BYTES + ((((c >> 3) ^ swz_v<CPR>(r)) << 4) | ((c & 7) << 1)));
     };
     bf16x8 pb[RTW];
 #pragma unroll
@@ -443,15 +519,28 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       const bf16x4 hi4 = __builtin_shufflevector(pk[rt][1][0], pk[rt][1][1], 0, 1, 2, 3);
       pb[rt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-#pragma unroll
-    for (int cb = 0; cb < CBW; ++cb) {
-      const int c0 = (cw * CBW + cb) * 16;
-      const bf16x4 lo4 = vt4(g4 * 4, c0);
-      const bf16x4 hi4 = vt4(16 + g4 * 4, c0);
+    constexpr int HI = 16 * ROW_BYTES;
+    auto pv = [&](int cb, bf16x4 lo4, bf16x4 hi4) {
       const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
         o[rt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], o[rt][cb], 0, 0, 0);
+    };
+    if constexpr (CBW % 2 == 0) {
+#pragma unroll
+      for (int cb = 0; cb < CBW; cb += 2) {
+        bf16x4 l0, h0, l1, h1;
+        lds_read_tr16_x4<HI>(vt_addr(cb), vt_addr(cb + 1), l0, h0, l1, h1);
+        pv(cb, l0, h0);
+        pv(cb + 1, l1, h1);
+      }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < CBW; ++cb) {
+        bf16x4 l0, h0;
+        lds_read_tr16_x2<HI>(vt_addr(cb), l0, h0);
+        pv(cb, l0, h0);
+      }
     }
   };
 
@@ -489,12 +578,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   };
 
   // ---- 6. the pipeline ----
-  // prologue: tiles 0 .. NS-2 in flight, then the first segment's queries; one full
-  // wait covers both, so no wait for the query registers is left in the loop.
+  // prologue: tiles 0 .. AHEAD-1 in flight, then the first segment's queries; one
+  // full wait covers both, so no wait for the query registers is left in the loop.
   {
     Cursor c = issue;
 #pragma unroll
-    for (int f = 0; f < NS - 1; ++f) {
+    for (int f = 0; f < AHEAD; ++f) {
       if (f < count) {
         issue_tile(c, f);
         advance(c);
@@ -524,14 +613,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       begin_segment(cons);
       seg_from_start = true;
     } else {
-      const int after = count - 1 - f;  // tiles issued after this one: min(NS - 2, after)
-      if (after >= 2) wait_vm_and_sync<2 * LD>();
-      else if (after == 1) wait_vm_and_sync<LD>();
-      else wait_vm_and_sync<0>();
+      wait_tiles<LD, AHEAD - 1>(count - 1 - f);  // tiles issued after this one: min(AHEAD - 1, .)
     }
-    // the stage refilled next was consumed in the previous step by every wave
-    if (f + NS - 1 < count) {
-      issue_tile(issue, f + NS - 1);
+    // the stage refilled next was last read at step f + AHEAD - NS <= f - 1, which
+    // every wave has finished (the barrier above)
+    if (f + AHEAD < count) {
+      issue_tile(issue, f + AHEAD);
       advance(issue);
     }
     const unsigned char* ks = smem + (f % NS) * C::STAGE_BYTES;
