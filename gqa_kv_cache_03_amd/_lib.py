@@ -27,6 +27,7 @@ GQA_POLICY_MFMA = 2
 EXPORTED = (
     "gqa_decode_opts_init",
     "gqa_decode",
+    "gqa_decode_append",
     "gqa_decode_plan",
     "gqa_decode_workspace_size",
     "gqa_status_string",
@@ -107,6 +108,9 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float,
                              vp, ctypes.POINTER(DecodeOpts)]
     L.gqa_decode.restype = i32
+    L.gqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float,
+                                    vp, ctypes.POINTER(DecodeOpts)]
+    L.gqa_decode_append.restype = i32
     L.gqa_decode_plan.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(DecodeOpts), ctypes.POINTER(Plan)]
     L.gqa_decode_plan.restype = i32
     L.gqa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(DecodeOpts),

@@ -25,6 +25,7 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
+    "-fvisibility=hidden",
     "-Wall",
     "-Wno-unused-function",
     "-Wno-unused-command-line-argument",

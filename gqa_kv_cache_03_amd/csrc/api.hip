@@ -183,6 +183,89 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
   return GQA_OK;
 }
 
+// Shared by gqa_decode (k_new == v_new == nullptr) and gqa_decode_append.
+int decode_impl(const void* q, const void* k_new, const void* v_new, const void* k_cache,
+                const void* v_cache, const int32_t* seq_lens, const int32_t* block_table, void* out,
+                int B, int H, int G, int d_h, int q_len, float scale, void* stream,
+                const gqa_decode_opts* opts) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !out || !opts) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(seq_lens, 4) || (block_table && !aligned(block_table, 4)))
+    return GQA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+  if (opts->struct_size >= sizeof(gqa_decode_opts) && !block_table && opts->page_size != 0)
+    return GQA_ERR_INVALID_ARGUMENT;
+  const bool paged = block_table != nullptr;
+  Plan p;
+  int st = make_plan(B, H, G, d_h, q_len, opts, paged, /*query_device=*/false, &p);
+  if (st != GQA_OK) return st;
+  st = make_plan(B, H, G, d_h, q_len, opts, paged, /*query_device=*/true, &p);
+  if (st != GQA_OK) return st;
+  const gqa_plan& pl = p.pub;
+  if (pl.workspace_bytes > 0) {
+    if (!opts->workspace || !aligned(opts->workspace, kWsAlign) ||
+        opts->workspace_bytes < pl.workspace_bytes)
+      return GQA_ERR_WORKSPACE;
+  }
+
+  DecodeParams dp{};
+  dp.q = q;
+  dp.k = k_cache;
+  dp.v = v_cache;
+  dp.k_new = k_new;
+  dp.v_new = v_new;
+  dp.seq_lens = seq_lens;
+  dp.table = block_table;
+  dp.out = out;
+  if (pl.workspace_bytes > 0) {
+    unsigned char* ws = static_cast<unsigned char*>(opts->workspace);
+    dp.ws_o = reinterpret_cast<float*>(ws);
+    dp.ws_lse = reinterpret_cast<float*>(ws + p.ws_o_bytes);
+    dp.ws_prefix = reinterpret_cast<int32_t*>(ws + p.ws_o_bytes + p.ws_lse_bytes);
+  }
+  dp.B = B;
+  dp.H = H;
+  dp.G = G;
+  dp.q_len = q_len;
+  dp.hpg = H / G;
+  dp.R = pl.rows;
+  dp.capacity = pl.capacity;
+  dp.page_shift = p.paged ? p.page_shift : 0;
+  dp.max_blocks = p.paged ? opts->max_blocks_per_seq : 0;
+  dp.num_pages = p.paged ? opts->num_pages : 0;
+  dp.chunk = pl.chunk_tokens;
+  dp.max_splits = pl.max_splits;
+  dp.causal = opts->causal;
+  dp.row_block = p.row_block;
+  dp.n_row_blocks = pl.row_blocks;
+  dp.nwg = pl.workgroups;
+  dp.qk_scale_log2 = scale * 1.4426950408889634f;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(opts->profile_events));
+  if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return GQA_ERR_HIP;
+  const dim3 grid(pl.grid[0], pl.grid[1], pl.grid[2]);
+  if (k_new && pl.policy != GQA_POLICY_MFMA) {
+    // the vector-ALU kernel reads every key from the cache: write the new rows first
+    if (gqa::launch_append(dp, opts->dtype == GQA_DTYPE_BF16 ? 2 : 4, d_h, p.paged, s) != hipSuccess)
+      return GQA_ERR_HIP;
+  }
+  hipError_t e = (pl.policy == GQA_POLICY_MFMA)
+                     ? gqa::launch_decode_mfma(dp, opts->dtype, d_h, p.paged, grid, s)
+                     : gqa::launch_decode_valu(dp, opts->dtype, d_h, p.paged, grid, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return GQA_ERR_HIP;
+  if (pl.policy == GQA_POLICY_MFMA) {
+    e = gqa::launch_merge_persistent(dp, d_h, s);
+    if (e != hipSuccess) return GQA_ERR_HIP;
+  } else if (pl.max_splits > 1) {
+    e = gqa::launch_merge(dp, opts->dtype, d_h, s);
+    if (e != hipSuccess) return GQA_ERR_HIP;
+  }
+  if (ev[2] && hipEventRecord(ev[2], s) != hipSuccess) return GQA_ERR_HIP;
+  return GQA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -236,75 +319,17 @@ int gqa_decode_workspace_size(int B, int H, int G, int d_h, int q_len, const gqa
 int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                const int32_t* block_table, void* out, int B, int H, int G, int d_h, int q_len,
                float scale, void* stream, const gqa_decode_opts* opts) {
-  if (!q || !k_cache || !v_cache || !seq_lens || !out || !opts) return GQA_ERR_INVALID_ARGUMENT;
-  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
-      !aligned(seq_lens, 4) || (block_table && !aligned(block_table, 4)))
-    return GQA_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
-  if (opts->struct_size >= sizeof(gqa_decode_opts) && !block_table && opts->page_size != 0)
-    return GQA_ERR_INVALID_ARGUMENT;
-  const bool paged = block_table != nullptr;
-  Plan p;
-  int st = make_plan(B, H, G, d_h, q_len, opts, paged, /*query_device=*/false, &p);
-  if (st != GQA_OK) return st;
-  st = make_plan(B, H, G, d_h, q_len, opts, paged, /*query_device=*/true, &p);
-  if (st != GQA_OK) return st;
-  const gqa_plan& pl = p.pub;
-  if (pl.workspace_bytes > 0) {
-    if (!opts->workspace || !aligned(opts->workspace, kWsAlign) ||
-        opts->workspace_bytes < pl.workspace_bytes)
-      return GQA_ERR_WORKSPACE;
-  }
+  return decode_impl(q, nullptr, nullptr, k_cache, v_cache, seq_lens, block_table, out, B, H, G, d_h,
+                     q_len, scale, stream, opts);
+}
 
-  DecodeParams dp{};
-  dp.q = q;
-  dp.k = k_cache;
-  dp.v = v_cache;
-  dp.seq_lens = seq_lens;
-  dp.table = block_table;
-  dp.out = out;
-  if (pl.workspace_bytes > 0) {
-    unsigned char* ws = static_cast<unsigned char*>(opts->workspace);
-    dp.ws_o = reinterpret_cast<float*>(ws);
-    dp.ws_lse = reinterpret_cast<float*>(ws + p.ws_o_bytes);
-    dp.ws_prefix = reinterpret_cast<int32_t*>(ws + p.ws_o_bytes + p.ws_lse_bytes);
-  }
-  dp.B = B;
-  dp.H = H;
-  dp.G = G;
-  dp.q_len = q_len;
-  dp.hpg = H / G;
-  dp.R = pl.rows;
-  dp.capacity = pl.capacity;
-  dp.page_shift = p.paged ? p.page_shift : 0;
-  dp.max_blocks = p.paged ? opts->max_blocks_per_seq : 0;
-  dp.num_pages = p.paged ? opts->num_pages : 0;
-  dp.chunk = pl.chunk_tokens;
-  dp.max_splits = pl.max_splits;
-  dp.causal = opts->causal;
-  dp.row_block = p.row_block;
-  dp.n_row_blocks = pl.row_blocks;
-  dp.nwg = pl.workgroups;
-  dp.qk_scale_log2 = scale * 1.4426950408889634f;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(opts->profile_events));
-  if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return GQA_ERR_HIP;
-  const dim3 grid(pl.grid[0], pl.grid[1], pl.grid[2]);
-  hipError_t e = (pl.policy == GQA_POLICY_MFMA)
-                     ? gqa::launch_decode_mfma(dp, opts->dtype, d_h, p.paged, grid, s)
-                     : gqa::launch_decode_valu(dp, opts->dtype, d_h, p.paged, grid, s);
-  if (e != hipSuccess) return GQA_ERR_HIP;
-  if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return GQA_ERR_HIP;
-  if (pl.policy == GQA_POLICY_MFMA) {
-    e = gqa::launch_merge_persistent(dp, d_h, s);
-    if (e != hipSuccess) return GQA_ERR_HIP;
-  } else if (pl.max_splits > 1) {
-    e = gqa::launch_merge(dp, opts->dtype, d_h, s);
-    if (e != hipSuccess) return GQA_ERR_HIP;
-  }
-  if (ev[2] && hipEventRecord(ev[2], s) != hipSuccess) return GQA_ERR_HIP;
-  return GQA_OK;
+int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                      const int32_t* seq_lens, const int32_t* block_table, void* out, int B, int H,
+                      int G, int d_h, int q_len, float scale, void* stream,
+                      const gqa_decode_opts* opts) {
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return GQA_ERR_INVALID_ARGUMENT;
+  return decode_impl(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table, out, B, H, G, d_h, q_len,
+                     scale, stream, opts);
 }
 
 }  // extern "C"

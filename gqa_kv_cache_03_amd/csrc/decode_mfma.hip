@@ -347,34 +347,87 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const int pmask = (1 << pshift) - 1;
 
   // ---- 2. staging: tile f of this workgroup goes to ring stage f % NS ----
+  // Cache append (k_new set): positions new0 = L - q_len .. L - 1 are the new tokens,
+  // read from k_new / v_new [B, q_len, G, D] instead of the cache (which does not
+  // hold them yet); copy_new_rows writes them into the cache once they are in LDS.
+  const unsigned char* __restrict__ kn = static_cast<const unsigned char*>(p.k_new);
+  const unsigned char* __restrict__ vn = static_cast<const unsigned char*>(p.v_new);
+  auto tile_has_new = [&](const Cursor& c) { return kn != nullptr && c.t * T + T > c.L - p.q_len; };
+
+  auto cache_row = [&](const Cursor& c, const int* pg, int row, int j) -> size_t {
+    if constexpr (PAGED) {
+      return (((size_t)pg[row >> 4] * p.G + c.g) * (size_t)(pmask + 1) + (j & pmask)) * ROW_BYTES;
+    } else {
+      return (((size_t)c.b * p.G + c.g) * (size_t)p.capacity + j) * ROW_BYTES;
+    }
+  };
+  auto tile_pages = [&](const Cursor& c, int* pg) {
+    if constexpr (PAGED) {
+      const int32_t* trow = p.table + (size_t)c.b * p.max_blocks;
+      const int t0 = c.t * T;
+#pragma unroll
+      for (int gi = 0; gi < T / 16; ++gi) {
+        int page = load_uniform_i32(trow, min(t0 + gi * 16, c.L - 1) >> pshift);
+        pg[gi] = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
+      }
+    }
+  };
+
   auto issue_tile = [&](const Cursor& c, int f) {
     unsigned char* st = smem + (f % NS) * C::STAGE_BYTES;
     const int t0 = c.t * T;
     const int end = c.L;
+    const int new0 = end - p.q_len;
+    const bool has_new = tile_has_new(c);
     int pg[T / 16] = {};
-    if constexpr (PAGED) {
-      const int32_t* trow = p.table + (size_t)c.b * p.max_blocks;
-#pragma unroll
-      for (int gi = 0; gi < T / 16; ++gi) {
-        int page = load_uniform_i32(trow, min(t0 + gi * 16, end - 1) >> pshift);
-        pg[gi] = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
-      }
-    }
-    const size_t seq_base = PAGED ? 0 : ((size_t)c.b * p.G + c.g) * (size_t)p.capacity * ROW_BYTES;
+    tile_pages(c, pg);
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) {
       const int qi = n * kThreads + tid;
       const int row = qi / CPR, pch = qi % CPR;
       const int j = min(t0 + row, end - 1);  // past the end: re-read the last row (masked)
-      size_t rb;
-      if constexpr (PAGED) {
-        rb = (((size_t)pg[row >> 4] * p.G + c.g) * (size_t)(pmask + 1) + (j & pmask)) * ROW_BYTES;
-      } else {
-        rb = seq_base + (size_t)j * ROW_BYTES;
+      const size_t rb = cache_row(c, pg, row, j);
+      const unsigned char* ksrc = kg + rb;
+      const unsigned char* vsrc = vg + rb;
+      if (has_new) {
+        asm volatile("");  // keep this a branch: only tiles holding new tokens pay for it
+        if (j >= new0) {
+          const size_t nb = (((size_t)c.b * p.q_len + (j - new0)) * p.G + c.g) * ROW_BYTES;
+          ksrc = kn + nb;
+          vsrc = vn + nb;
+        }
       }
       const int lds_off = n * kThreads * 16 + wave * 1024;  // this wave's 64 x 16 B slots
-      load16_to_lds(kg + rb + ((pch ^ swz_k<CPR>(row)) << 4), st + lds_off);
-      load16_to_lds(vg + rb + ((pch ^ swz_v<CPR>(row)) << 4), st + C::TENSOR_BYTES + lds_off);
+      load16_to_lds(ksrc + ((pch ^ swz_k<CPR>(row)) << 4), st + lds_off);
+      load16_to_lds(vsrc + ((pch ^ swz_v<CPR>(row)) << 4), st + C::TENSOR_BYTES + lds_off);
+    }
+  };
+
+  // Writes the new tokens' rows of staged tile f (already in LDS: every lane reads
+  // back the chunks its own loads placed) into the cache. Called right after the
+  // tile's wait, while nothing else is in flight.
+  auto copy_new_rows = [&](const Cursor& c, int f) {
+    if (!tile_has_new(c)) return;
+    const unsigned char* st = smem + (f % NS) * C::STAGE_BYTES;
+    const int t0 = c.t * T;
+    const int new0 = c.L - p.q_len;
+    unsigned char* kc = static_cast<unsigned char*>(const_cast<void*>(p.k));
+    unsigned char* vc = static_cast<unsigned char*>(const_cast<void*>(p.v));
+    int pg[T / 16] = {};
+    tile_pages(c, pg);
+#pragma unroll
+    for (int n = 0; n < LOADS; ++n) {
+      const int qi = n * kThreads + tid;
+      const int row = qi / CPR, pch = qi % CPR;
+      const int j = t0 + row;
+      if (j >= new0 && j < c.L) {  // a new token's row (not a re-read past the end)
+        const int slot = n * kThreads * 16 + wave * 1024 + lane * 16;
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(st + slot);
+        const u32x4 vv = *reinterpret_cast<const u32x4*>(st + C::TENSOR_BYTES + slot);
+        const size_t rb = cache_row(c, pg, row, j);
+        *reinterpret_cast<u32x4*>(kc + rb + ((pch ^ swz_k<CPR>(row)) << 4)) = kv;
+        *reinterpret_cast<u32x4*>(vc + rb + ((pch ^ swz_v<CPR>(row)) << 4)) = vv;
+      }
     }
   };
 
@@ -615,6 +668,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     } else {
       wait_tiles<LD, AHEAD - 1>(count - 1 - f);  // tiles issued after this one: min(AHEAD - 1, .)
     }
+    // new tokens' rows of this tile go to the cache before the next tile is issued,
+    // so their LDS read-back waits for nothing else
+    copy_new_rows(cons, f);
     // the stage refilled next was last read at step f + AHEAD - NS <= f - 1, which
     // every wave has finished (the barrier above)
     if (f + AHEAD < count) {

@@ -11,6 +11,8 @@ struct DecodeParams {
   const void* q;           // [B, q_len, H, D]
   const void* k;           // contiguous [B, G, cap, D] or paged [pages, G, P, D]
   const void* v;
+  const void* k_new;       // append: new tokens' K [B, q_len, G, D] (nullptr: none)
+  const void* v_new;       // append: new tokens' V
   const int32_t* seq_lens; // [B]
   const int32_t* table;    // [B, max_blocks] or nullptr
   void* out;               // [B, q_len, H, D]
@@ -45,6 +47,8 @@ hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int d_h, bool pa
                               dim3 grid, hipStream_t stream);
 hipError_t launch_merge(const DecodeParams& p, int dtype, int d_h, hipStream_t stream);
 hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t stream);
+// Writes k_new / v_new into the cache rows of the new tokens (vector-ALU path).
+hipError_t launch_append(const DecodeParams& p, int elem_bytes, int d_h, bool paged, hipStream_t stream);
 
 // Geometry of the MFMA kernel variants, chosen by packed row count R.
 struct MfmaVariant {

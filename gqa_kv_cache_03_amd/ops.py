@@ -80,8 +80,34 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, block_table=None, *, scale: Option
     num_splits: MFMA policy -- persistent workgroups (0: what the device holds);
     VALU policy -- maximum context splits per sequence (0: heuristic).
     """
+    return _call(q, None, None, k_cache, v_cache, seq_lens, block_table, scale=scale, out=out,
+                 causal=causal, num_splits=num_splits, chunk_tokens=chunk_tokens, policy=policy,
+                 workspace=workspace, profile_events=profile_events)
+
+
+def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table=None, *,
+                      scale: Optional[float] = None, out=None, causal: bool = True, num_splits: int = 0,
+                      chunk_tokens: int = 0, policy: str = "auto", workspace=None, profile_events=None):
+    """gqa_decode fused with writing the new tokens' K/V into the cache.
+
+    k_new/v_new [B, q_len, G, d_h]: row t of sequence b is written at cache position
+    seq_lens[b] - q_len + t (paged: through block_table, pages already allocated);
+    the step then attends over the updated cache. Returns `out`.
+    """
+    return _call(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table, scale=scale, out=out,
+                 causal=causal, num_splits=num_splits, chunk_tokens=chunk_tokens, policy=policy,
+                 workspace=workspace, profile_events=profile_events)
+
+
+def _call(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table, *, scale, out, causal, num_splits,
+          chunk_tokens, policy, workspace, profile_events):
     import torch
-    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)):
+    tensors = [("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)]
+    if k_new is not None or v_new is not None:
+        tensors += [("k_new", k_new), ("v_new", v_new)]
+    for name, t in tensors:
+        if t is None:
+            raise ValueError(f"{name} is required")
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
@@ -98,6 +124,10 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, block_table=None, *, scale: Option
     B, q_len, H, d, G, geo = _geometry(q, k_cache, block_table)
     if seq_lens.numel() != B:
         raise ValueError("seq_lens must have B entries")
+    if k_new is not None:
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            if tuple(t.shape) != (B, q_len, G, d) or t.dtype != q.dtype:
+                raise ValueError(f"{name} must be [B, q_len, G, d_h] = {(B, q_len, G, d)} in q's dtype")
     code = _dtype_code(torch, q.dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -121,11 +151,16 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, block_table=None, *, scale: Option
         for i, ev in enumerate(profile_events):
             o.profile_events[i] = ev
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = L.gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
-                      None if block_table is None else block_table.data_ptr(), out.data_ptr(),
-                      B, H, G, d, q_len, ctypes.c_float(scale), stream, ctypes.byref(o))
+    bt = None if block_table is None else block_table.data_ptr()
+    if k_new is None:
+        st = L.gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), bt,
+                          out.data_ptr(), B, H, G, d, q_len, ctypes.c_float(scale), stream, ctypes.byref(o))
+    else:
+        st = L.gqa_decode_append(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+                                 v_cache.data_ptr(), seq_lens.data_ptr(), bt, out.data_ptr(), B, H, G, d,
+                                 q_len, ctypes.c_float(scale), stream, ctypes.byref(o))
     if st != _lib.GQA_OK:
-        raise GqaError(st)
+        raise GqaError(st, "gqa_decode" if k_new is None else "gqa_decode_append")
     return out
 
 

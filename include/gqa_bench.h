@@ -16,6 +16,9 @@
 extern "C" {
 #endif
 
+/* the library is built with hidden visibility; these are its exported symbols */
+#pragma GCC visibility push(default)
+
 /*
  * gqa_bench_read_stream -- read `bytes` bytes of device memory at `buf` (16-byte
  * aligned, bytes a multiple of 16) with coalesced 16-byte loads and write one
@@ -24,6 +27,8 @@ extern "C" {
  * Returns a gqa_status (INVALID_ARGUMENT for NULL/misaligned pointers or sizes).
  */
 int gqa_bench_read_stream(const void* buf, size_t bytes, void* sink, void* stream);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

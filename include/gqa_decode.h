@@ -25,7 +25,8 @@
  *  - Return value: a gqa_status (0 = success). Nothing is thrown or aborted across
  *    the ABI. Every argument check runs on the host before any HIP call.
  *  - Device arrays are row-major, contiguous, 16-byte aligned, owned by the caller.
- *  - The library keeps no state between calls and never allocates memory.
+ *  - The library never allocates memory; the only state it keeps between calls is a
+ *    per-device cache of the compute-unit count.
  */
 #ifndef GQA_DECODE_H
 #define GQA_DECODE_H
@@ -36,6 +37,9 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* the library is built with hidden visibility; these are its exported symbols */
+#pragma GCC visibility push(default)
 
 #define GQA_ABI_VERSION 1
 
@@ -132,6 +136,33 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache,
                int B, int H, int G, int d_h, int q_len, float scale,
                void* stream, const gqa_decode_opts* opts);
 
+/*
+ * gqa_decode_append -- the same decode step, fused with writing the q_len new tokens'
+ * keys and values into the cache (asynchronous on `stream`). Each step of
+ * autoregressive decoding appends its tokens' K/V to the cache and then attends over
+ * the whole cache: the cache traffic that bounds decoding ("The KV-Cache Bandwidth
+ * Wall", llms.blog GQA/MQA page); paged caches keep those rows in fixed-size blocks
+ * ("PagedAttention", same page).
+ *
+ *   k_new, v_new [B, q_len, G, d_h] (dtype): K and V of the new tokens, row t of
+ *                sequence b being cache position seq_lens[b] - q_len + t.
+ *   k_cache, v_cache  written at those positions (contiguous: [b, g, pos]; paged:
+ *                page block_table[b][pos / P], slot pos % P, which the caller has
+ *                allocated), read everywhere else; no other cache byte is written.
+ *   Everything else is as for gqa_decode, whose result this equals when called on
+ *   the cache after the append.
+ *
+ * k_new and v_new must be 16-byte aligned and must not alias the cache or out. On
+ * the matrix-core path the new rows are read straight from k_new/v_new and copied
+ * into the cache by the kernel that attends over them (one launch plus the merge);
+ * on the vector-ALU path a copy kernel runs first. Errors are those of gqa_decode
+ * plus INVALID_ARGUMENT for NULL or misaligned k_new / v_new.
+ */
+int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                      void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
+                      void* out, int B, int H, int G, int d_h, int q_len, float scale,
+                      void* stream, const gqa_decode_opts* opts);
+
 /* The plan gqa_decode would use for these sizes (validation included). */
 int gqa_decode_plan(int B, int H, int G, int d_h, int q_len,
                     const gqa_decode_opts* opts, gqa_plan* plan);
@@ -142,6 +173,8 @@ int gqa_decode_workspace_size(int B, int H, int G, int d_h, int q_len,
 
 const char* gqa_status_string(int status);
 int gqa_abi_version(void);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }

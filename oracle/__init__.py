@@ -11,6 +11,7 @@ from .gqa_oracle import (  # noqa: F401
     visible_keys,
     kv_rows,
     gqa_decode,
+    append_kv,
     kv_bytes,
     touched_kv_rows,
 )

@@ -129,6 +129,35 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale: float, G: int,
     return out
 
 
+def append_kv(cache, new, seq_lens, block_table=None, page_size: int = 0):
+    """The cache after a step's new tokens are added to it, as a float64 copy.
+
+    Keys and values are projections of the memory positions and, during incremental
+    decoding, live in a cache with one row per position (llms.blog page,
+    "Multi-Query Attention" > "Mathematical Formulation"); every step then rereads
+    the whole cache ("The KV-Cache Bandwidth Wall"). Reading: the step's q_len new
+    tokens occupy the last q_len of the seq_lens[b] positions, so row t of
+    new[b, :, g] (new is [B, q_len, G, d]) becomes position seq_lens[b] - q_len + t of
+    KV head g -- cache[b, g, pos] when contiguous, or slot pos % page_size of page
+    block_table[b, pos // page_size] when paged ("PagedAttention"). No other row
+    changes.
+    """
+    out = np.array(cache, dtype=np.float64, copy=True)
+    new = np.asarray(new, dtype=np.float64)
+    B, q_len, G, d = new.shape
+    for b in range(B):
+        L = int(seq_lens[b])
+        assert q_len <= L, "every new token must be in the cache"
+        for t in range(q_len):
+            pos = L - q_len + t
+            for g in range(G):
+                if block_table is None:
+                    out[b, g, pos] = new[b, t, g]
+                else:
+                    out[int(block_table[b, pos // page_size]), g, pos % page_size] = new[b, t, g]
+    return out
+
+
 def kv_bytes(G: int, d_h: int, itemsize: int, seq_lens) -> int:
     """K and V bytes one decode step must read when each group is read once:
     2 * G * d_h * itemsize * sum_b L_b. With uniform lengths n this is the

@@ -204,3 +204,24 @@ def test_bench_helper_validation():
     assert L.gqa_bench_read_stream(None, 16, P, None) == INV
     assert L.gqa_bench_read_stream(P, 15, P, None) == INV
     assert L.gqa_bench_read_stream(P + 4, 16, P, None) == INV
+
+
+def call_append(kn=P, vn=P, **kw):
+    o = kw.pop("o", None) or opts()
+    args = dict(B=2, H=8, G=2, d=128, q_len=1, scale=0.1, q=P, k=P, v=P, sl=P, bt=None, out=P)
+    args.update(kw)
+    return _lib.lib().gqa_decode_append(args["q"], kn, vn, args["k"], args["v"], args["sl"], args["bt"],
+                                        args["out"], args["B"], args["H"], args["G"], args["d"], args["q_len"],
+                                        ctypes.c_float(args["scale"]), None, ctypes.byref(o))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), INV), (dict(vn=None), INV), (dict(kn=P + 8), INV), (dict(vn=P + 2), INV),
+    (dict(q=None), INV), (dict(H=8, G=3), INV), (dict(d=96), UNS),
+])
+def test_append_invalid_arguments_are_rejected(kw, status):
+    assert call_append(**kw) == status
+
+
+def test_append_workspace_checked():
+    assert call_append(o=opts(num_splits=7)) == WS

@@ -415,3 +415,76 @@ def test_planted_page_slot_mistake_is_caught(monkeypatch):
     ref = O.gqa_decode(q, pk, pv, lens, 0.6, 2, block_table=tbl, page_size=3)
     bf = brute_force_decimal(q, pk, pv, lens, 0.6, 2, block_table=tbl, P=3)
     assert not np.allclose(ref, bf, rtol=0, atol=1e-6)
+
+
+# --------------------------------------------- cache append (the step's new tokens)
+
+def _append_case(rng, paged_P=0):
+    B, H, G, d, q_len = 3, 8, 2, 8, 3
+    lens = np.array([5, 3, 11], dtype=np.int32)
+    old_lens = lens - q_len
+    cap = 14
+    old_k = rng.standard_normal((B, G, cap, d))
+    old_v = rng.standard_normal((B, G, cap, d))
+    for b in range(B):                       # rows of this step and beyond: not yet written
+        old_k[b, :, old_lens[b]:] = np.nan
+        old_v[b, :, old_lens[b]:] = np.nan
+    k_new = rng.standard_normal((B, q_len, G, d))
+    v_new = rng.standard_normal((B, q_len, G, d))
+    q = rng.standard_normal((B, q_len, H, d))
+    return q, old_k, old_v, k_new, v_new, lens, old_lens, G
+
+
+def _concatenated(old, new, old_lens, lens):
+    """Expected cache, built independently: each sequence's old rows followed by its
+    new tokens (np.concatenate along positions), padded with NaN."""
+    B, G, cap, d = old.shape
+    full = np.full_like(old, np.nan)
+    for b in range(B):
+        rows = np.concatenate([old[b, :, :old_lens[b]], new[b].transpose(1, 0, 2)], axis=1)
+        assert rows.shape[1] == lens[b]
+        full[b, :, :lens[b]] = rows
+    return full
+
+
+def test_append_places_new_rows_after_the_old_ones():
+    q, ok, ov, kn, vn, lens, old_lens, G = _append_case(np.random.default_rng(81))
+    k = oracle.append_kv(ok, kn, lens)
+    exp = _concatenated(ok, kn, old_lens, lens)
+    for b in range(len(lens)):
+        np.testing.assert_array_equal(k[b, :, :lens[b]], exp[b, :, :lens[b]])
+        assert np.isnan(k[b, :, lens[b]:]).all()          # nothing past the sequence
+    assert np.isnan(ok[0, :, old_lens[0]:]).all()          # the input is not modified
+
+
+def test_append_then_decode_equals_decode_on_concatenated_cache():
+    q, ok, ov, kn, vn, lens, old_lens, G = _append_case(np.random.default_rng(82))
+    got = oracle.gqa_decode(q, oracle.append_kv(ok, kn, lens), oracle.append_kv(ov, vn, lens), lens, 0.4, G)
+    ref = oracle.gqa_decode(q, _concatenated(ok, kn, old_lens, lens), _concatenated(ov, vn, old_lens, lens),
+                            lens, 0.4, G)
+    np.testing.assert_array_equal(got, ref)
+
+
+@pytest.mark.parametrize("P", [2, 4])
+def test_append_paged_equals_contiguous(P):
+    rng = np.random.default_rng(83)
+    q, ok, ov, kn, vn, lens, old_lens, G = _append_case(rng)
+    zk = np.nan_to_num(ok, nan=0.0)
+    pool, table = paginate_np(np.random.default_rng(5), zk, lens, P)   # pages for all lens rows
+    pool_after = oracle.append_kv(pool, kn, lens, block_table=table, page_size=P)
+    contig_after = oracle.append_kv(zk, kn, lens)
+    for b in range(len(lens)):
+        for j in range(lens[b]):
+            np.testing.assert_array_equal(pool_after[table[b, j // P], :, j % P], contig_after[b, :, j])
+
+
+def test_planted_append_position_mistake_is_caught():
+    q, ok, ov, kn, vn, lens, old_lens, G = _append_case(np.random.default_rng(84))
+    wrong = np.array(ok, copy=True)
+    for b in range(len(lens)):                  # off by one: the new rows one slot late
+        for t in range(kn.shape[1]):
+            pos = lens[b] - kn.shape[1] + t + 1
+            if pos < ok.shape[2]:
+                wrong[b, :, pos] = kn[b, t]
+    exp = _concatenated(ok, kn, old_lens, lens)
+    assert not all(np.array_equal(wrong[b, :, :lens[b]], exp[b, :, :lens[b]]) for b in range(len(lens)))
