@@ -1,16 +1,17 @@
 #!/usr/bin/env python3
-"""Single-GPU benchmark of one GQA decode step (the split-K decode kernel + LSE merge).
+"""Single-GPU benchmark of one GQA decode step (the decode kernel + LSE merge).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--append]
 
-A step is one gqa_decode call over the whole batch of the workload, inputs resident in
-HBM. Several copies of the KV cache are rotated so that every step reads cold data
+A step is one gqa_decode call (gqa_decode_append with --append) over the whole batch
+of the workload, inputs resident in HBM. Several copies of the KV cache are rotated so that every step reads cold data
 (the 256 MiB Infinity Cache cannot serve a step from the previous one). Prints one
 JSON line:
 
   value      KV GB/s = 2 * G * d_h * itemsize * sum(seq_lens) / (time per step)
-  roofline   the split-K decode kernel's own duration (HIP events on the launch
-             stream) against MI355X's 8 TB/s HBM peak
+  roofline   the decode kernel's algorithmic bytes over its own duration (HIP events
+             recorded by the library on the launch stream) against MI355X's 8 TB/s
+             HBM peak
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -56,12 +57,15 @@ def load_traffic(workload: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # enough warm-up for the clocks to settle: a fresh process's first few steps run slow
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--policy", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--append", action="store_true",
+                    help="time gqa_decode_append: the step also writes the new tokens' K/V into the cache")
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies rotated (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -153,7 +157,7 @@ def main():
     import numpy as np
     import torch
 
-    from gqa_kv_cache_03_amd import gqa_decode, plan, read_stream
+    from gqa_kv_cache_03_amd import gqa_decode, gqa_decode_append, plan, read_stream
     from gqa_synth import BENCH_DEFAULT, make_inputs, workload
 
     name = args.workload or BENCH_DEFAULT
@@ -176,9 +180,28 @@ def main():
               chunk_tokens=args.chunk, policy=args.policy)
     ws = torch.empty(max(pl["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
 
+    new_bytes = 0
+    if args.append:
+        # the new tokens' rows, as the projections would hand them over: [B, q_len, G, d_h]
+        k_new = torch.empty((wl.B, wl.q_len, wl.G, wl.d_h), dtype=inp.q.dtype, device=dev)
+        v_new = torch.empty_like(k_new)
+        for b in range(wl.B):
+            for t in range(wl.q_len):
+                pos = int(inp.lens[b]) - wl.q_len + t
+                if inp.block_table is None:
+                    k_new[b, t], v_new[b, t] = inp.k_cache[b, :, pos], inp.v_cache[b, :, pos]
+                else:
+                    pg, sl = int(inp.table[b, pos // wl.page_size]), pos % wl.page_size
+                    k_new[b, t], v_new[b, t] = inp.k_cache[pg, :, sl], inp.v_cache[pg, :, sl]
+        new_bytes = 2 * k_new.numel() * k_new.element_size()
+
     def step(i, events=None):
-        gqa_decode(inp.q, ks[i % copies], vs[i % copies], inp.seq_lens, inp.block_table, out=out,
-                   workspace=ws, profile_events=events, **kw)
+        if args.append:
+            gqa_decode_append(inp.q, k_new, v_new, ks[i % copies], vs[i % copies], inp.seq_lens,
+                              inp.block_table, out=out, workspace=ws, profile_events=events, **kw)
+        else:
+            gqa_decode(inp.q, ks[i % copies], vs[i % copies], inp.seq_lens, inp.block_table, out=out,
+                       workspace=ws, profile_events=events, **kw)
 
     for i in range(args.warmup):
         step(i)
@@ -214,7 +237,9 @@ def main():
 
     q_bytes = inp.q.numel() * inp.q.element_size()
     tbl_bytes = 0 if inp.table is None else 4 * int(sum(-(-int(L) // wl.page_size) for L in inp.lens))
-    dec_alg_bytes = kv_bytes + q_bytes + tbl_bytes
+    # with the append, the new rows are read from k_new/v_new instead of the cache (same
+    # count) and written to the cache once
+    dec_alg_bytes = kv_bytes + q_bytes + tbl_bytes + new_bytes
     achieved = dec_alg_bytes / (dec_ms * 1e-3) / 1e9
 
     ceiling = None
@@ -250,7 +275,7 @@ def main():
         "dtype": "bf16" if wl.dtype == "bfloat16" else "f32",
         "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and block tables)",
         "config": {
-            "workload": name,
+            "workload": name + (" +append" if args.append else ""),
             "B": wl.B, "H": wl.H, "G": wl.G, "d_h": wl.d_h, "q_len": wl.q_len,
             "layout": wl.layout, "page_size": wl.page_size or None,
             "lengths": [wl.len_lo, wl.len_hi], "sum_seq_lens": int(inp.lens.sum()),
@@ -266,7 +291,7 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(name),
+            "traffic": load_traffic(name + ("_append" if args.append else "")),
             "kernel": "decode_mfma_kernel" if pl["policy"] == "mfma" else "decode_valu_kernel",
             "algorithmic_bytes_per_launch": int(dec_alg_bytes),
         },
