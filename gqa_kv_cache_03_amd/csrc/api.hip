@@ -17,7 +17,8 @@ namespace {
 
 using gqa::DecodeParams;
 
-constexpr int kMaxRows = 256;
+constexpr int kMaxRows = 1024;        // packed rows per KV group (H/G * q_len)
+constexpr int kMfmaBlockRows = 256;   // packed rows one MFMA workgroup holds
 constexpr int kTargetSlots = 8192;   // split-kernel workgroup slots the VALU heuristic aims for
 constexpr size_t kWsAlign = 256;
 constexpr int kMfmaTile = 32;        // keys per tile of the persistent MFMA schedule
@@ -102,12 +103,17 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
   pub.block_threads = 256;
 
   if (policy == GQA_POLICY_MFMA) {
-    // Persistent balanced schedule: the (sequence, group) segments, cut into 32-key
-    // tiles and laid end to end, are shared equally by every workgroup the device
-    // holds at once; num_splits > 0 forces the workgroup count instead.
-    const long long max_tiles = (long long)B * G * ((capacity + kMfmaTile - 1) / kMfmaTile);
+    // Persistent balanced schedule: the (sequence, group, row block) segments, cut
+    // into 32-key tiles and laid end to end, are shared equally by every workgroup the
+    // device holds at once; num_splits > 0 forces the workgroup count instead. A group
+    // with more packed rows than one workgroup holds is split into equal row blocks,
+    // each a segment that reads the group's K/V (at that size the step is bound by the
+    // matrix cores, not by the extra reads).
+    const int n_rb = (int)((R + kMfmaBlockRows - 1) / kMfmaBlockRows);
+    const int rb_rows = n_rb == 1 ? (int)R : (int)(((R + n_rb - 1) / n_rb + 15) / 16 * 16);
+    const long long max_tiles = (long long)B * G * n_rb * ((capacity + kMfmaTile - 1) / kMfmaTile);
     if (max_tiles > INT32_MAX / 2) return GQA_ERR_UNSUPPORTED;
-    const gqa::MfmaVariant v = gqa::mfma_variant_for_rows((int)R, d_h, paged, query_device);
+    const gqa::MfmaVariant v = gqa::mfma_variant_for_rows(rb_rows, d_h, paged, query_device);
     int nwg = opts->num_splits;
     if (nwg == 0) {
       // two per CU measured fastest; fewer when the variant's registers or LDS allow
@@ -117,7 +123,8 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
     }
     if (nwg > (1 << 20)) return GQA_ERR_UNSUPPORTED;
     pub.schedule = 1;
-    pub.row_blocks = 1;
+    pub.row_blocks = n_rb;
+    p.row_block = rb_rows;
     pub.tile_tokens = kMfmaTile;
     pub.chunk_tokens = 0;
     pub.max_splits = 2;
@@ -126,7 +133,7 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
     pub.grid[1] = 1;
     pub.grid[2] = 1;
     pub.lds_bytes = v.lds_bytes;
-    const size_t prow = (size_t)nwg * 2 * (size_t)R;
+    const size_t prow = (size_t)nwg * 2 * (size_t)rb_rows;
     p.ws_o_bytes = round_up(prow * d_h * sizeof(float), kWsAlign);
     p.ws_lse_bytes = round_up(prow * sizeof(float), kWsAlign);
     pub.workspace_bytes = p.ws_o_bytes + p.ws_lse_bytes + round_up(((size_t)B + 1) * sizeof(int32_t), kWsAlign);

@@ -254,9 +254,10 @@ struct MfmaCfg {
   static_assert(LDS_BYTES >= (kThreads + 8) * 4, "start-up scratch fits in the ring");
 };
 
-// Position in the flattened tile sequence: segment (b, g), tile t of n, length L.
+// Position in the flattened tile sequence: segment (b, g, rb) -- row block rb of KV
+// group g of sequence b -- tile t of n, sequence length L.
 struct Cursor {
-  int b, g, t, n, L;
+  int b, g, rb, t, n, L;
 };
 
 template <int D, int NRW, int NCW, int RTW, bool PAGED>
@@ -276,8 +277,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const int w = blockIdx.x;
 
   // ---- 1. this workgroup's share of the flattened tile sequence ----
-  // Tiles per segment of sequence b: n_b = ceil(L_b / T); the G segments of b are
-  // consecutive. Every wave scans seq_lens (a few hundred bytes) on its own, with
+  // Tiles per segment of sequence b: n_b = ceil(L_b / T). A KV group's R packed rows
+  // form n_row_blocks blocks of at most row_block rows (one block unless R exceeds
+  // what a workgroup's registers hold); each block is a segment of its own that reads
+  // the group's K/V. The GS = G * n_row_blocks segments of b are consecutive. Every wave scans seq_lens (a few hundred bytes) on its own, with
   // cross-lane operations only (no LDS, no barrier), to find the total W and the
   // segment holding its workgroup's first tile; the first wave of workgroup 0 also
   // publishes the per-sequence prefix sums for the merge kernel.
@@ -287,7 +290,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const int bb = b0 + lane;
     total += wave_sum_i32(bb < p.B ? (clamp_len(p.seq_lens[bb], p.capacity) + T - 1) / T : 0);
   }
-  const int W = p.G * __builtin_amdgcn_readfirstlane(total);  // the planner bounds it to fit int32
+  const int GS = p.G * p.n_row_blocks;  // segments per sequence
+  const int W = GS * __builtin_amdgcn_readfirstlane(total);  // the planner bounds it to fit int32
   const int lo = (int)(((long long)w * W) / p.nwg);
   const int hi = (int)(((long long)(w + 1) * W) / p.nwg);
   const bool publish = w == 0 && wave == 0;
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   for (int b0 = 0; b0 < p.B; b0 += 64) {
     const int bb = b0 + lane;
     const int L = b0 == 0 ? L0 : (bb < p.B ? clamp_len(p.seq_lens[bb], p.capacity) : 0);
-    const int gn = L > 0 ? p.G * ((L + T - 1) / T) : 0;
+    const int gn = L > 0 ? GS * ((L + T - 1) / T) : 0;
     const int incl = carry + wave_incl_scan_i32(gn);
     const int excl = incl - gn;
     if (publish && bb < p.B) p.ws_prefix[bb] = excl;
@@ -323,19 +327,26 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   issue.b = b_start;
   issue.L = L_start;
   issue.n = (issue.L + T - 1) / T;
-  issue.g = (lo - pre_start) / issue.n;
-  issue.t = (lo - pre_start) - issue.g * issue.n;
+  {
+    const int seg = (lo - pre_start) / issue.n;
+    issue.g = seg / p.n_row_blocks;
+    issue.rb = seg - issue.g * p.n_row_blocks;
+    issue.t = (lo - pre_start) - seg * issue.n;
+  }
   Cursor cons = issue;
 
   auto advance = [&](Cursor& c) {
     if (++c.t == c.n) {
       c.t = 0;
-      if (++c.g == p.G) {
-        c.g = 0;
-        ++c.b;
-        if (c.b < p.B) {
-          c.L = clamp_len(load_uniform_i32(p.seq_lens, c.b), p.capacity);
-          c.n = (c.L + T - 1) / T;
+      if (++c.rb == p.n_row_blocks) {
+        c.rb = 0;
+        if (++c.g == p.G) {
+          c.g = 0;
+          ++c.b;
+          if (c.b < p.B) {
+            c.L = clamp_len(load_uniform_i32(p.seq_lens, c.b), p.capacity);
+            c.n = (c.L + T - 1) / T;
+          }
         }
       }
     }
@@ -445,7 +456,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       l_run[rt] = 0.f;
 #pragma unroll
       for (int cb = 0; cb < CBW; ++cb) o[rt][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      int r = (rw * RTW + rt) * 16 + l16;
+      int r = c.rb * p.row_block + (rw * RTW + rt) * 16 + l16;
       r = r < p.R ? r : p.R - 1;
       lim[rt] = p.causal ? (c.L - p.q_len + r / p.hpg) : (c.L - 1);  // last visible key
     }
@@ -458,12 +469,18 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const float qk_c = fmaxf(fabsf(p.qk_scale_log2), 1e-30f);
   const unsigned q_sign = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;  // negative scale: flip q
 
-  // packed query rows of segment (b, g), as B operands of S^T = K Q^T
+  // row r_local of a segment's block is packed row rb * row_block + r_local of its group
+  auto packed_row = [&](const Cursor& c, int r_local) -> int {
+    const int r = c.rb * p.row_block + r_local;
+    return (r_local < p.row_block && r < p.R) ? r : -1;
+  };
+
+  // packed query rows of segment (b, g, rb), as B operands of S^T = K Q^T
   auto load_q = [&](const Cursor& c) {
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-      const int r = (rw * RTW + rt) * 16 + l16;
-      if (r < p.R) {
+      const int r = packed_row(c, (rw * RTW + rt) * 16 + l16);
+      if (r >= 0) {
         const int t = r / p.hpg;
         const int h = c.g * p.hpg + (r - t * p.hpg);
         const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)(c.b * p.q_len + t) * p.H + h) * D;
@@ -606,12 +623,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       const float l = wave_sum_across_groups(l_run[rt]);
       const float inv = (l > 0.f) ? 1.f / l : 0.f;
       const float lse = (l > 0.f) ? m_run[rt] + __log2f(l) : kNegInf;
-      const int r = (rw * RTW + rt) * 16 + l16;
-      if (r < p.R) {
+      const int r_local = (rw * RTW + rt) * 16 + l16;
+      const int r = packed_row(c, r_local);
+      if (r >= 0) {
         const int t = r / p.hpg;
         const int h = c.g * p.hpg + (r - t * p.hpg);
         const size_t orow = (size_t)c.b * rows_per_b + (size_t)t * p.H + h;
-        const size_t prow = ((size_t)w * 2 + slot) * p.R + r;
+        const size_t prow = ((size_t)w * 2 + slot) * p.row_block + r_local;
 #pragma unroll
         for (int cb = 0; cb < CBW; ++cb) {
           const int col = (cw * CBW + cb) * 16 + g4 * 4;
@@ -720,7 +738,7 @@ int variant_occupancy(bool paged) {
 template <int D>
 hipError_t launch_for_rows(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream) {
 #define X(ROWS, NRW, NCW, RTW) \
-  if (p.R <= ROWS) return launch_variant<D, NRW, NCW, RTW>(p, paged, grid, stream);
+  if (p.row_block <= ROWS) return launch_variant<D, NRW, NCW, RTW>(p, paged, grid, stream);
   GQA_MFMA_VARIANTS(X)
 #undef X
   return hipErrorInvalidValue;

@@ -15,8 +15,8 @@
 // across waves through LDS.
 //
 // Persistent schedule: the decode kernel's workgroups share one flat sequence of
-// key tiles (segment (b, g) = the n_b tiles of sequence b and KV group g, segments
-// in (b, g) order). Workgroup w owns tiles [lo(w), hi(w)), lo(w) = floor(w W / nwg).
+// key tiles (segment (b, g, rb) = the n_b tiles of sequence b for row block rb of KV
+// group g, segments in (b, g, rb) order). Workgroup w owns tiles [lo(w), hi(w)), lo(w) = floor(w W / nwg).
 // A segment inside one workgroup was written straight to the output; a segment cut
 // by workgroup boundaries left one partial per workgroup it touches: in the
 // workgroup's slot 0 if the segment holds the workgroup's first tile, else in
@@ -150,15 +150,20 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
   __shared__ float sm_l[NGRP];
   __shared__ f32x4 sm_o[NGRP][LPR];
 
-  const int seg = blockIdx.x / p.R;
-  const int r = blockIdx.x - seg * p.R;
-  const int b = seg / p.G;
-  const int g = seg - b * p.G;
+  const int RB = p.row_block;                     // rows per segment
+  const int GS = p.G * p.n_row_blocks;            // segments per sequence
+  const int seg = blockIdx.x / RB;
+  const int r_local = blockIdx.x - seg * RB;
+  const int b = seg / GS;
+  const int gs = seg - b * GS;
+  const int g = gs / p.n_row_blocks;
+  const int r = (gs - g * p.n_row_blocks) * RB + r_local;  // packed row of group g
+  if (r >= p.R) return;
   const int W = p.ws_prefix[p.B];
   const int pre = p.ws_prefix[b];
-  const int n = (p.ws_prefix[b + 1] - pre) / p.G;  // tiles per segment of b
+  const int n = (p.ws_prefix[b + 1] - pre) / GS;  // tiles per segment of b
   if (n <= 0 || W <= 0) return;
-  const int s0 = pre + g * n;
+  const int s0 = pre + gs * n;
   const int wa = tile_owner(s0, W, p.nwg);
   const int wb = tile_owner(s0 + n - 1, W, p.nwg);
   if (wa == wb) return;  // written whole by one workgroup
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
       lse[u] = kNegInf;
       v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (w <= wb && tile_lo(w, W, p.nwg) < tile_lo(w + 1, W, p.nwg)) {  // else empty
-        const size_t prow = ((size_t)w * kPersistSlots + (w == wa ? slot_a : 0)) * p.R + r;
+        const size_t prow = ((size_t)w * kPersistSlots + (w == wa ? slot_a : 0)) * RB + r_local;
         lse[u] = p.ws_lse[prow];
         v[u] = *reinterpret_cast<const f32x4*>(p.ws_o + prow * D + c);
       }
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
 
 template <int D>
 hipError_t go_persistent(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid(p.B * p.G * p.R);
+  const dim3 grid(p.B * p.G * p.n_row_blocks * p.row_block);
   hipLaunchKernelGGL((merge_persistent_kernel<D>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }

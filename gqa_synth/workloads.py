@@ -105,6 +105,20 @@ for _w in [
         description="paged cache, 16-token pages, permuted block table, lengths U[8192, 65536]",
     ),
     _c5(1), _c5(2), _c5(4), _c5(8), _c5(32),
+    # verification of 16 drafted tokens against the cache, in 32-token pages: the
+    # MQA case packs 16 x 32 = 512 query rows per KV group
+    Workload(
+        name="spec16_paged32_bf16_B8_H32_G1_d128_n32k",
+        B=8, H=32, G=1, d_h=128, q_len=16, dtype="bfloat16",
+        len_lo=32768 + 16, len_hi=32768 + 16, layout="paged", page_size=32, seed=1006,
+        description="16 new tokens (causal among them), MQA, 32-token pages",
+    ),
+    Workload(
+        name="spec16_paged32_bf16_B8_H32_G4_d128_n32k",
+        B=8, H=32, G=4, d_h=128, q_len=16, dtype="bfloat16",
+        len_lo=32768 + 16, len_hi=32768 + 16, layout="paged", page_size=32, seed=1007,
+        description="16 new tokens (causal among them), G=4, 32-token pages",
+    ),
 ]:
     WORKLOADS[_w.name] = _w
 

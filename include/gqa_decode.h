@@ -46,7 +46,7 @@ extern "C" {
 typedef enum gqa_status {
   GQA_OK = 0,
   GQA_ERR_INVALID_ARGUMENT = 1, /* a NULL/misaligned pointer, a bad size, H % G != 0 ... */
-  GQA_ERR_UNSUPPORTED = 2,      /* valid but not compiled: d_h not 64/128, R > 256, ... */
+  GQA_ERR_UNSUPPORTED = 2,      /* valid but not compiled: d_h not 64/128, R > 1024, ... */
   GQA_ERR_WORKSPACE = 3,        /* the plan needs split-K scratch the caller did not give */
   GQA_ERR_HIP = 4               /* a HIP launch or event call failed */
 } gqa_status;
@@ -85,7 +85,10 @@ typedef struct gqa_plan {
   int32_t schedule;           /* 0: split-K grid (splits, G*row_blocks, B);
                                  1: persistent balanced workgroups (grid[0] of them) */
   int32_t rows;               /* R = (H/G) * q_len query rows per KV group */
-  int32_t row_blocks;         /* workgroups that share one (b, g, split) along rows */
+  int32_t row_blocks;         /* split-K grid: workgroups that share one (b, g, split)
+                                 along rows; persistent: row blocks per KV group (a
+                                 group of more than 256 packed rows is split into equal
+                                 blocks, each reading the group's K/V) */
   int32_t tile_tokens;        /* keys staged per pipeline step */
   int32_t chunk_tokens;       /* split-K grid: keys per context split; else 0 */
   int32_t max_splits;         /* split-K grid: ceil(capacity / chunk_tokens);
@@ -126,7 +129,7 @@ void gqa_decode_opts_init(gqa_decode_opts* opts);
  *
  * Errors: INVALID_ARGUMENT for NULL or misaligned pointers, non-positive sizes,
  * H % G != 0, non-finite scale, a bad opts struct or paged geometry; UNSUPPORTED for
- * d_h not in {64,128}, an unknown dtype, R = (H/G)*q_len > 256, a forced MFMA
+ * d_h not in {64,128}, an unknown dtype, R = (H/G)*q_len > 1024, a forced MFMA
  * policy with fp32 or sizes whose tile counts overflow int32; WORKSPACE when the
  * plan needs workspace (gqa_decode_workspace_size) and it is NULL, too small or not
  * 256-byte aligned; HIP when a launch or event record fails.

@@ -100,7 +100,7 @@ def plan(B=2, H=8, G=2, d=128, q_len=1, o=None):
     (dict(H=8, G=3), INV), (dict(H=4, G=8), INV),
     (dict(scale=float("nan")), INV), (dict(scale=float("inf")), INV),
     (dict(d=96), UNS), (dict(d=256), UNS),
-    (dict(H=64, G=1, q_len=5), UNS),                  # R = 320 > 256
+    (dict(H=64, G=1, q_len=17), UNS),                 # R = 1088 > 1024
     (dict(o=False), INV),
 ])
 def test_invalid_arguments_are_rejected(kw, status):
@@ -168,7 +168,7 @@ def test_plan_policy_and_workspace_formula():
 @pytest.mark.parametrize("nwg", [1, 5, 600])
 def test_persistent_plan_and_workspace_formula(nwg):
     """MFMA policy: num_splits is the persistent workgroup count; each holds two
-    partial slots of R rows, plus B + 1 prefix sums."""
+    partial slots of R rows (one row block here), plus B + 1 prefix sums."""
     B, H, G, q_len, d = 3, 16, 4, 2, 128
     st, pl = plan(B=B, H=H, G=G, q_len=q_len, d=d, o=opts(cache_capacity=1000, num_splits=nwg))
     assert st == OK and pl.policy == _lib.GQA_POLICY_MFMA and pl.schedule == 1
@@ -184,12 +184,15 @@ def test_persistent_default_fills_the_device():
     assert pl.workgroups == 512
 
 
-@pytest.mark.parametrize("R", [1, 2, 3, 4, 8, 16, 17, 32, 64, 65, 128, 256])
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 8, 16, 17, 32, 64, 65, 128, 256, 257, 300, 512, 520, 1024])
 def test_every_row_count_up_to_the_maximum_plans(R):
     st, pl = plan(H=R, G=1, q_len=1, o=opts(cache_capacity=1 << 16))
     assert st == OK and pl.rows == R
     assert pl.policy == (_lib.GQA_POLICY_MFMA if R >= 4 else _lib.GQA_POLICY_VALU)
     assert pl.lds_bytes <= 160 * 1024
+    if pl.policy == _lib.GQA_POLICY_MFMA:
+        # row blocks of at most 256 rows that together cover R
+        assert pl.row_blocks == -(-R // 256)
 
 
 def test_status_strings():
@@ -225,3 +228,14 @@ def test_append_invalid_arguments_are_rejected(kw, status):
 
 def test_append_workspace_checked():
     assert call_append(o=opts(num_splits=7)) == WS
+
+
+def test_row_blocks_split_large_groups_evenly():
+    """R = 16 tokens x 32 heads = 512 rows: two blocks of 256; R = 300: two of 160;
+    the partial slots hold one block's rows."""
+    for q_len, H, rb_rows in ((16, 32, 256), (10, 30, 160)):
+        st, pl = plan(B=2, H=H, G=1, q_len=q_len, o=opts(cache_capacity=4096, num_splits=64))
+        R = H * q_len
+        assert st == OK and pl.row_blocks == -(-R // 256)
+        assert pl.row_blocks * rb_rows >= R and rb_rows % 16 == 0
+        assert pl.workspace_bytes == ro(64 * 2 * rb_rows * 128 * 4) + ro(64 * 2 * rb_rows * 4) + ro(3 * 4)

@@ -55,6 +55,10 @@ CASES = [
     (2, 24, 4, 128, 2, [100, 701], "bfloat16", 0),     # R = 12
     (2, 8, 2, 64, 2, [90, 260], "bfloat16", 0),        # d = 64 on MFMA
     (2, 32, 1, 64, 4, [90, 1000], "bfloat16", 16),     # d = 64, R = 128, paged
+    (1, 32, 1, 128, 16, [1500], "bfloat16", 0),        # R = 512: two row blocks of 256
+    (2, 30, 1, 128, 10, [900, 40], "bfloat16", 32),    # R = 300: two blocks of 160, paged 32
+    (2, 64, 1, 64, 9, [300, 50], "bfloat16", 0),       # R = 576: three blocks of 192, d = 64
+    (2, 32, 2, 128, 12, [700, 64], "bfloat16", 32),    # q_len 12, R = 192, paged 32
 ]
 
 
@@ -69,7 +73,8 @@ def test_matches_oracle(B, H, G, d, q_len, lens, dtype, page, splits):
     assert_parity(got, ref, dtype, f"{wl.name} splits={splits}")
 
 
-@pytest.mark.parametrize("R_case", [(32, 8, 1, 4), (32, 4, 1, 4), (32, 2, 4, 2), (32, 1, 4, 2), (64, 1, 4, 2)])
+@pytest.mark.parametrize("R_case", [(32, 8, 1, 4), (32, 4, 1, 4), (32, 2, 4, 2), (32, 1, 4, 2), (64, 1, 4, 2),
+                                    (32, 1, 16, 2)])
 @pytest.mark.parametrize("nwg", [1, 2, 5, 64, 333, 5000])
 def test_persistent_boundaries(R_case, nwg):
     """Persistent workgroup counts from one (every segment inside one workgroup, many
