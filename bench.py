@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "GQA decode KV GB/s (% of MI355X HBM peak) and tokens/s at 1 GPU"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak (no sparsity)
 KERNEL_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "gqa_internal.h")
 
 
@@ -261,6 +262,14 @@ def main():
         del buf
 
     value = kv_bytes / (ms * 1e-3) / 1e9
+    # useful matrix work of the decode kernel: QK^T and PV, 2 * 2 * d_h flop per
+    # (query row, visible key) -- counted over all L keys (the causal triangle among
+    # the q_len new tokens is a negligible correction)
+    flops = 4 * wl.H * wl.q_len * wl.d_h * int(sum(int(L) for L in inp.lens))
+    tflops = flops / (dec_ms * 1e-3) / 1e12
+    intensity = flops / dec_alg_bytes
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    mfma_bound = pl["policy"] == "mfma" and intensity > ridge
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -286,15 +295,19 @@ def main():
         "read_ceiling_gbps": None if ceiling is None else round(ceiling, 1),
         "kernel_ms": {"split_decode": round(dec_ms, 6), "lse_merge": round(mrg_ms, 6)},
         "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "bound": "mfma" if mfma_bound else "hbm",
+            "achieved": round(tflops, 2) if mfma_bound else round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
+            "unit": "TFLOP/s" if mfma_bound else "GB/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS if mfma_bound else achieved / HBM_PEAK_GBPS, 4),
             "traffic": load_traffic(name + ("_append" if args.append else "")),
             "kernel": "decode_mfma_kernel" if pl["policy"] == "mfma" else "decode_valu_kernel",
             "algorithmic_bytes_per_launch": int(dec_alg_bytes),
+            "flops_per_launch": int(flops),
+            "flop_per_byte": round(intensity, 2),
+            "hbm_gbps": round(achieved, 2),
         },
+        "mfma_util": None if pl["policy"] != "mfma" else round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "cpu_baseline": None,
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 6),
     }

@@ -51,6 +51,10 @@ class DecodeOpts(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("profile_events", ctypes.c_void_p * 3),
+        ("head_group", ctypes.c_void_p),
+        ("max_group_heads", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32),
+        ("head_active", ctypes.c_void_p),
     ]
 
 

@@ -19,6 +19,7 @@ using gqa::DecodeParams;
 
 constexpr int kMaxRows = 1024;        // packed rows per KV group (H/G * q_len)
 constexpr int kMfmaBlockRows = 256;   // packed rows one MFMA workgroup holds
+constexpr int kMaxMappedHeads = 256;  // query heads a head -> group map may cover
 constexpr int kTargetSlots = 8192;   // split-kernel workgroup slots the VALU heuristic aims for
 constexpr size_t kWsAlign = 256;
 constexpr int kMfmaTile = 32;        // keys per tile of the persistent MFMA schedule
@@ -62,14 +63,25 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
               bool query_device, Plan* out) {
   if (!opts || opts->struct_size < sizeof(gqa_decode_opts)) return GQA_ERR_INVALID_ARGUMENT;
   if (B <= 0 || H <= 0 || G <= 0 || d_h <= 0 || q_len <= 0) return GQA_ERR_INVALID_ARGUMENT;
-  if (G > H || H % G != 0) return GQA_ERR_INVALID_ARGUMENT;
+  // grouping variants: a call-time head -> KV head map and a per-(token, head) active
+  // mask (matrix-core path only)
+  const bool head_map = opts->head_group != nullptr;
+  const bool variant = head_map || opts->head_active != nullptr;
+  if (G > H || (!head_map && H % G != 0)) return GQA_ERR_INVALID_ARGUMENT;
+  if (opts->reserved0 != 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (opts->max_group_heads < 0 || opts->max_group_heads > H) return GQA_ERR_INVALID_ARGUMENT;
+  if (head_map && !aligned(opts->head_group, 4)) return GQA_ERR_INVALID_ARGUMENT;
   if (opts->dtype != GQA_DTYPE_F32 && opts->dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  if (variant && (opts->dtype != GQA_DTYPE_BF16 || opts->policy == GQA_POLICY_VALU || H > kMaxMappedHeads))
+    return GQA_ERR_UNSUPPORTED;
   if (d_h != 64 && d_h != 128) return GQA_ERR_UNSUPPORTED;
   if (opts->causal != 0 && opts->causal != 1) return GQA_ERR_INVALID_ARGUMENT;
   if (opts->num_splits < 0 || opts->chunk_tokens < 0) return GQA_ERR_INVALID_ARGUMENT;
   if (opts->policy < GQA_POLICY_AUTO || opts->policy > GQA_POLICY_MFMA) return GQA_ERR_INVALID_ARGUMENT;
 
-  const int hpg = H / G;
+  // packed rows per KV group: H/G heads x q_len tokens, or the largest group a head
+  // map may form
+  const int hpg = head_map ? (opts->max_group_heads > 0 ? opts->max_group_heads : H) : H / G;
   const long long R = (long long)hpg * q_len;
   if (R > kMaxRows) return GQA_ERR_UNSUPPORTED;
   if ((long long)B * q_len * H > INT32_MAX / 256) return GQA_ERR_UNSUPPORTED;
@@ -93,7 +105,7 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
 
   int policy = opts->policy;
   if (policy == GQA_POLICY_AUTO)
-    policy = (opts->dtype == GQA_DTYPE_BF16 && R >= 4) ? GQA_POLICY_MFMA : GQA_POLICY_VALU;
+    policy = (opts->dtype == GQA_DTYPE_BF16 && (R >= 4 || variant)) ? GQA_POLICY_MFMA : GQA_POLICY_VALU;
   if (policy == GQA_POLICY_MFMA && opts->dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
 
   gqa_plan& pub = p.pub;
@@ -234,7 +246,9 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const void*
   dp.H = H;
   dp.G = G;
   dp.q_len = q_len;
-  dp.hpg = H / G;
+  dp.hpg = opts->head_group ? 1 : H / G;  // unused with a head map (groups are counted)
+  dp.head_group = opts->head_group;
+  dp.head_active = opts->head_active;
   dp.R = pl.rows;
   dp.capacity = pl.capacity;
   dp.page_shift = p.paged ? p.page_shift : 0;

@@ -448,6 +448,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   f32x4 o[RTW][CBW];
   int lim[RTW];
   int lim_min = 0;
+  // query (token, head) of this lane's packed row in each row tile of the current
+  // segment (-1: a padding row), and whether that pair is active
+  int row_t[RTW], row_h[RTW];
+  bool row_on[RTW];
 
   auto begin_segment = [&](const Cursor& c) {
 #pragma unroll
@@ -456,9 +460,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       l_run[rt] = 0.f;
 #pragma unroll
       for (int cb = 0; cb < CBW; ++cb) o[rt][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      int r = c.rb * p.row_block + (rw * RTW + rt) * 16 + l16;
-      r = r < p.R ? r : p.R - 1;
-      lim[rt] = p.causal ? (c.L - p.q_len + r / p.hpg) : (c.L - 1);  // last visible key
+      // padding rows take the last token's limit (their results are discarded)
+      const int t = row_t[rt] >= 0 ? row_t[rt] : p.q_len - 1;
+      lim[rt] = p.causal ? (c.L - p.q_len + t) : (c.L - 1);  // last visible key
     }
     lim_min = p.causal ? (c.L - p.q_len) : (c.L - 1);
   };
@@ -469,20 +473,72 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const float qk_c = fmaxf(fabsf(p.qk_scale_log2), 1e-30f);
   const unsigned q_sign = p.qk_scale_log2 < 0.f ? 0x80008000u : 0u;  // negative scale: flip q
 
-  // row r_local of a segment's block is packed row rb * row_block + r_local of its group
-  auto packed_row = [&](const Cursor& c, int r_local) -> int {
-    const int r = c.rb * p.row_block + r_local;
-    return (r_local < p.row_block && r < p.R) ? r : -1;
+  // Packed rows of a segment: row r of KV group g is query token t = r / n_g of the
+  // group's (r % n_g)-th query head, n_g heads in ascending order. Contiguous groups
+  // (no head map): n_g = H/G, heads g*n_g ... A head map (non-uniform groups) is read
+  // with one ballot per 64 heads; a lane then finds its head as the k-th set bit.
+  auto map_rows = [&](const Cursor& c) {
+    int n_g = p.hpg;
+    unsigned long long gm[4] = {0ull, 0ull, 0ull, 0ull};
+    if (p.head_group) {
+      n_g = 0;
+#pragma unroll
+      for (int ch = 0; ch < 4; ++ch) {
+        const int h = ch * 64 + lane;
+        const bool in = h < p.H && p.head_group[h] == c.g;
+        gm[ch] = __builtin_amdgcn_ballot_w64(in);
+        n_g += __builtin_popcountll(gm[ch]);
+      }
+    }
+    const int R_g = n_g * p.q_len;
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt) {
+      const int r_local = (rw * RTW + rt) * 16 + l16;
+      const int r = c.rb * p.row_block + r_local;
+      row_t[rt] = -1;
+      row_h[rt] = 0;
+      if (r_local < p.row_block && r < R_g) {
+        const int t = r / n_g;
+        const int k = r - t * n_g;
+        int h = c.g * n_g + k;
+        if (p.head_group) {
+          int before = 0;
+          h = 0;
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch) {
+            const int cnt = __builtin_popcountll(gm[ch]);
+            if (k >= before && k < before + cnt) {
+              // position of set bit (k - before) of gm[ch], by binary search on
+              // prefix popcounts
+              const int want = k - before;
+              int pos = 0;
+#pragma unroll
+              for (int step = 32; step >= 1; step >>= 1) {
+                const unsigned long long below = (1ull << (pos + step)) - 1ull;
+                if (__builtin_popcountll(gm[ch] & below) <= want) pos += step;
+              }
+              h = ch * 64 + pos;
+            }
+            before += cnt;
+          }
+        }
+        row_t[rt] = t;
+        row_h[rt] = h;
+      }
+      row_on[rt] = row_t[rt] >= 0 &&
+                   (p.head_active == nullptr ||
+                    p.head_active[((size_t)c.b * p.q_len + row_t[rt]) * p.H + row_h[rt]] != 0);
+    }
   };
 
   // packed query rows of segment (b, g, rb), as B operands of S^T = K Q^T
   auto load_q = [&](const Cursor& c) {
+    map_rows(c);
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
-      const int r = packed_row(c, (rw * RTW + rt) * 16 + l16);
-      if (r >= 0) {
-        const int t = r / p.hpg;
-        const int h = c.g * p.hpg + (r - t * p.hpg);
+      if (row_t[rt] >= 0) {
+        const int t = row_t[rt];
+        const int h = row_h[rt];
         const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)(c.b * p.q_len + t) * p.H + h) * D;
 #pragma unroll
         for (int cc = 0; cc < CC; ++cc) {
@@ -620,14 +676,15 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const size_t rows_per_b = (size_t)p.q_len * p.H;
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
+      // an inactive (token, head) pair writes zeros (and an empty partial)
       const float l = wave_sum_across_groups(l_run[rt]);
-      const float inv = (l > 0.f) ? 1.f / l : 0.f;
-      const float lse = (l > 0.f) ? m_run[rt] + __log2f(l) : kNegInf;
+      const bool live = l > 0.f && row_on[rt];
+      const float inv = live ? 1.f / l : 0.f;
+      const float lse = live ? m_run[rt] + __log2f(l) : kNegInf;
       const int r_local = (rw * RTW + rt) * 16 + l16;
-      const int r = packed_row(c, r_local);
-      if (r >= 0) {
-        const int t = r / p.hpg;
-        const int h = c.g * p.hpg + (r - t * p.hpg);
+      if (row_t[rt] >= 0) {
+        const int t = row_t[rt];
+        const int h = row_h[rt];
         const size_t orow = (size_t)c.b * rows_per_b + (size_t)t * p.H + h;
         const size_t prow = ((size_t)w * 2 + slot) * p.row_block + r_local;
 #pragma unroll

@@ -15,6 +15,8 @@ struct DecodeParams {
   const void* v_new;       // append: new tokens' V
   const int32_t* seq_lens; // [B]
   const int32_t* table;    // [B, max_blocks] or nullptr
+  const int32_t* head_group;   // [H] KV head of each query head, or nullptr: h / hpg
+  const uint8_t* head_active;  // [B, q_len, H]: 0 = (token, head) inactive (output 0), or nullptr
   void* out;               // [B, q_len, H, D]
   // split partials (normalised O, log2-domain log-sum-exp):
   //   split-K grid (VALU): ws_o [B, q_len, H, max_splits, D], ws_lse [B, q_len, H, max_splits]

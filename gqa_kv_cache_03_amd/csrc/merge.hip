@@ -149,6 +149,7 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
   __shared__ float sm_m[NGRP];
   __shared__ float sm_l[NGRP];
   __shared__ f32x4 sm_o[NGRP][LPR];
+  __shared__ unsigned long long sm_heads[kThreads / 64];
 
   const int RB = p.row_block;                     // rows per segment
   const int GS = p.G * p.n_row_blocks;            // segments per sequence
@@ -158,7 +159,37 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
   const int gs = seg - b * GS;
   const int g = gs / p.n_row_blocks;
   const int r = (gs - g * p.n_row_blocks) * RB + r_local;  // packed row of group g
-  if (r >= p.R) return;
+
+  // (token, head) of packed row r, as the decode kernel maps it: token r / n_g of the
+  // group's (r % n_g)-th head in ascending order (contiguous groups without a map)
+  int n_g = p.hpg;
+  if (p.head_group) {
+    const bool in = (int)threadIdx.x < p.H && p.head_group[threadIdx.x] == g;
+    const unsigned long long bits = __builtin_amdgcn_ballot_w64(in);
+    if ((threadIdx.x & 63) == 0) sm_heads[threadIdx.x >> 6] = bits;
+    __syncthreads();
+    n_g = 0;
+#pragma unroll
+    for (int wv = 0; wv < kThreads / 64; ++wv) n_g += __builtin_popcountll(sm_heads[wv]);
+  }
+  if (r >= n_g * p.q_len) return;
+  const int t = r / n_g;
+  const int kh = r - t * n_g;  // the row's head is the group's kh-th
+  int h = g * n_g + kh;
+  if (p.head_group) {
+    int seen = 0;
+    for (int wv = 0; wv < kThreads / 64; ++wv) {
+      unsigned long long bits = sm_heads[wv];
+      while (bits) {
+        if (seen == kh) h = wv * 64 + __builtin_ctzll(bits);
+        ++seen;
+        bits &= bits - 1;
+      }
+    }
+  }
+  const size_t orow = ((size_t)b * p.q_len + t) * p.H + h;
+  const bool on = p.head_active == nullptr || p.head_active[orow] != 0;
+
   const int W = p.ws_prefix[p.B];
   const int pre = p.ws_prefix[b];
   const int n = (p.ws_prefix[b + 1] - pre) / GS;  // tiles per segment of b
@@ -223,10 +254,7 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
     tot += wt * sm_o[k][tid];
     lt += wt * sm_l[k];
   }
-  const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
-  const int t = r / p.hpg;
-  const int h = g * p.hpg + (r - t * p.hpg);
-  const size_t orow = ((size_t)b * p.q_len + t) * p.H + h;
+  const float inv = (lt > 0.f && on) ? 1.f / lt : 0.f;
   put4<__bf16>(static_cast<__bf16*>(p.out) + orow * D + c, tot * inv);
 }
 

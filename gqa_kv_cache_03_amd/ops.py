@@ -25,7 +25,8 @@ def _dtype_code(torch, dt) -> int:
 
 def make_opts(*, dtype_code: int, causal: bool, capacity: int, page_size: int = 0,
               max_blocks: int = 0, num_pages: int = 0, num_splits: int = 0,
-              chunk_tokens: int = 0, policy: str = "auto") -> DecodeOpts:
+              chunk_tokens: int = 0, policy: str = "auto", head_group=None, max_group_heads: int = 0,
+              head_active=None) -> DecodeOpts:
     o = _lib.default_opts()
     o.dtype = dtype_code
     o.causal = 1 if causal else 0
@@ -36,6 +37,9 @@ def make_opts(*, dtype_code: int, causal: bool, capacity: int, page_size: int = 
     o.num_splits = num_splits
     o.chunk_tokens = chunk_tokens
     o.policy = _POLICIES[policy]
+    o.head_group = None if head_group is None else head_group.data_ptr()
+    o.max_group_heads = max_group_heads
+    o.head_active = None if head_active is None else head_active.data_ptr()
     return o
 
 
@@ -56,12 +60,13 @@ def _geometry(q, k_cache, block_table):
 
 
 def plan(q, k_cache, block_table=None, *, causal=True, num_splits=0, chunk_tokens=0,
-         policy="auto") -> dict:
+         policy="auto", head_group=None, max_group_heads: int = 0, head_active=None) -> dict:
     """What gqa_decode would launch for these tensors (no device work)."""
     import torch
     B, q_len, H, d, G, geo = _geometry(q, k_cache, block_table)
     o = make_opts(dtype_code=_dtype_code(torch, q.dtype), causal=causal, num_splits=num_splits,
-                  chunk_tokens=chunk_tokens, policy=policy, **geo)
+                  chunk_tokens=chunk_tokens, policy=policy, head_group=head_group,
+                  max_group_heads=max_group_heads, head_active=head_active, **geo)
     pl = Plan()
     st = _lib.lib().gqa_decode_plan(B, H, G, d, q_len, ctypes.byref(o), ctypes.byref(pl))
     if st != _lib.GQA_OK:
@@ -71,7 +76,8 @@ def plan(q, k_cache, block_table=None, *, causal=True, num_splits=0, chunk_token
 
 def gqa_decode(q, k_cache, v_cache, seq_lens, block_table=None, *, scale: Optional[float] = None,
                out=None, causal: bool = True, num_splits: int = 0, chunk_tokens: int = 0,
-               policy: str = "auto", workspace=None, profile_events=None):
+               policy: str = "auto", workspace=None, profile_events=None, head_group=None,
+               max_group_heads: int = 0, head_active=None):
     """One GQA decode step on the current HIP stream; returns `out`.
 
     q [B, q_len, H, d_h]; k_cache/v_cache [B, G, cap, d_h] (contiguous) or
@@ -79,15 +85,20 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, block_table=None, *, scale: Option
     seq_lens int32 [B] counting the q_len new tokens. scale defaults to 1/sqrt(d_h).
     num_splits: MFMA policy -- persistent workgroups (0: what the device holds);
     VALU policy -- maximum context splits per sequence (0: heuristic).
+    head_group: int32 [H] device tensor, the KV head of each query head (non-uniform
+    groups; max_group_heads bounds any group's size, 0 = H). head_active: uint8
+    [B, q_len, H] device tensor, 0 = that (token, head) is inactive and outputs 0.
     """
     return _call(q, None, None, k_cache, v_cache, seq_lens, block_table, scale=scale, out=out,
                  causal=causal, num_splits=num_splits, chunk_tokens=chunk_tokens, policy=policy,
-                 workspace=workspace, profile_events=profile_events)
+                 workspace=workspace, profile_events=profile_events, head_group=head_group,
+                 max_group_heads=max_group_heads, head_active=head_active)
 
 
 def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table=None, *,
                       scale: Optional[float] = None, out=None, causal: bool = True, num_splits: int = 0,
-                      chunk_tokens: int = 0, policy: str = "auto", workspace=None, profile_events=None):
+                      chunk_tokens: int = 0, policy: str = "auto", workspace=None, profile_events=None,
+                      head_group=None, max_group_heads: int = 0, head_active=None):
     """gqa_decode fused with writing the new tokens' K/V into the cache.
 
     k_new/v_new [B, q_len, G, d_h]: row t of sequence b is written at cache position
@@ -96,11 +107,13 @@ def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table=N
     """
     return _call(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table, scale=scale, out=out,
                  causal=causal, num_splits=num_splits, chunk_tokens=chunk_tokens, policy=policy,
-                 workspace=workspace, profile_events=profile_events)
+                 workspace=workspace, profile_events=profile_events, head_group=head_group,
+                 max_group_heads=max_group_heads, head_active=head_active)
 
 
 def _call(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table, *, scale, out, causal, num_splits,
-          chunk_tokens, policy, workspace, profile_events):
+          chunk_tokens, policy, workspace, profile_events, head_group=None, max_group_heads=0,
+          head_active=None):
     import torch
     tensors = [("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)]
     if k_new is not None or v_new is not None:
@@ -128,11 +141,19 @@ def _call(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table, *, scale, ou
         for name, t in (("k_new", k_new), ("v_new", v_new)):
             if tuple(t.shape) != (B, q_len, G, d) or t.dtype != q.dtype:
                 raise ValueError(f"{name} must be [B, q_len, G, d_h] = {(B, q_len, G, d)} in q's dtype")
+    if head_group is not None and (head_group.dtype != torch.int32 or tuple(head_group.shape) != (H,)
+                                   or not head_group.is_cuda or not head_group.is_contiguous()):
+        raise ValueError("head_group must be a contiguous int32 device tensor of H entries")
+    if head_active is not None and (head_active.dtype != torch.uint8 or not head_active.is_cuda
+                                    or tuple(head_active.shape) != (B, q_len, H)
+                                    or not head_active.is_contiguous()):
+        raise ValueError("head_active must be a contiguous uint8 device tensor [B, q_len, H]")
     code = _dtype_code(torch, q.dtype)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     o = make_opts(dtype_code=code, causal=causal, num_splits=num_splits, chunk_tokens=chunk_tokens,
-                  policy=policy, **geo)
+                  policy=policy, head_group=head_group, max_group_heads=max_group_heads,
+                  head_active=head_active, **geo)
     L = _lib.lib()
     need = ctypes.c_size_t(0)
     st = L.gqa_decode_workspace_size(B, H, G, d, q_len, ctypes.byref(o), ctypes.byref(need))

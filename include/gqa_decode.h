@@ -76,6 +76,23 @@ typedef struct gqa_decode_opts {
   size_t   workspace_bytes;
   void*    profile_events[3]; /* optional hipEvent_t: recorded on `stream` before the
                                  decode kernel, between it and the merge, after the merge */
+  /* Grouping variants (matrix-core policy, bf16, H <= 256; NULL/0 = plain GQA):
+   *  head_group   device int32 [H]: the KV head (in [0, G)) each query head reads, for
+   *               a non-uniform allocation of query heads to KV heads decided at call
+   *               time (key-norm driven KDGQA/DGQA, "Beyond Uniform Query
+   *               Distribution: Key-Driven Grouped Query Attention", Figure 1). H % G
+   *               need not be 0 then; a KV head may serve any number of query heads.
+   *  max_group_heads  with head_group: an upper bound on the query heads of any one
+   *               KV head (0: H); it sizes the packed tile. A larger group is an error
+   *               the device cannot report: its surplus heads are left unwritten.
+   *  head_active  device uint8 [B, q_len, H]: 0 marks a (token, head) pair that a
+   *               router left inactive (Grouped Query Experts: k query heads per token
+   *               and group); its output row is 0. Every K/V byte is still read: the
+   *               variant cuts query rows, not cache traffic. */
+  const int32_t* head_group;
+  int32_t  max_group_heads;
+  int32_t  reserved0;          /* 0 */
+  const uint8_t* head_active;
 } gqa_decode_opts;
 
 /* What the library will launch for a shape (no device work; with a GPU present the

@@ -58,8 +58,14 @@ def group_of_head(h: int, H: int, G: int) -> int:
     return h // (H // G)
 
 
-def heads_of_group(g: int, H: int, G: int) -> list[int]:
-    return [h for h in range(H) if group_of_head(h, H, G) == g]
+def heads_of_group(g: int, H: int, G: int, head_group=None) -> list[int]:
+    """Query heads that read KV head g: the contiguous block, or, with a call-time
+    map (one KV head index per query head; the key-norm driven, non-uniform
+    allocation of "Beyond Uniform Query Distribution: Key-Driven Grouped Query
+    Attention", Figure 1), every head the map sends to g, in ascending order."""
+    if head_group is None:
+        return [h for h in range(H) if group_of_head(h, H, G) == g]
+    return [h for h in range(H) if int(head_group[h]) == g]
 
 
 def visible_keys(L: int, q_len: int, t: int, causal: bool) -> int:
@@ -91,19 +97,27 @@ def kv_rows(cache, b: int, g: int, L: int, block_table=None, page_size: int = 0,
 
 def gqa_decode(q, k_cache, v_cache, seq_lens, scale: float, G: int,
                block_table=None, page_size: int = 0, causal: bool = True,
-               return_weights: bool = False, touched: set | None = None):
+               return_weights: bool = False, touched: set | None = None,
+               head_group=None, head_active=None):
     """Attention output for every (sequence, new token, query head).
 
     q        [B, q_len, H, d]  (any real dtype; upcast to float64)
     k_cache  [B, G, cap, d] contiguous, or [num_pages, G, page_size, d] paged
     v_cache  same layout as k_cache
     seq_lens [B] visible keys per sequence, counting the q_len new tokens
+    head_group  optional [H] KV head of each query head (non-uniform groups)
+    head_active optional [B, q_len, H]; 0 marks a (token, head) pair left inactive by a
+             per-token router over each group's query heads (Grouped Query Experts,
+             thelatestinai page), whose output is 0: the pair is not computed
     returns  out [B, q_len, H, d] float64 (and, if asked, a dict of weights
              {(b, t, h): w[visible]}).
     """
     q = np.asarray(q, dtype=np.float64)
     B, q_len, H, d = q.shape
-    assert G >= 1 and H % G == 0, "query heads must split evenly into KV groups"
+    if head_group is None:
+        assert G >= 1 and H % G == 0, "query heads must split evenly into KV groups"
+    else:
+        assert len(head_group) == H and all(0 <= int(x) < G for x in head_group)
     scale = float(np.float32(scale))
     out = np.empty((B, q_len, H, d), dtype=np.float64)
     weights = {} if return_weights else None
@@ -113,7 +127,7 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale: float, G: int,
         for g in range(G):
             K = kv_rows(k_cache, b, g, L, block_table, page_size, touched)
             V = kv_rows(v_cache, b, g, L, block_table, page_size, touched)
-            for h in heads_of_group(g, H, G):
+            for h in heads_of_group(g, H, G, head_group):
                 Qh = q[b, :, h, :]                       # [q_len, d]
                 logits = scale * (Qh @ K.T)              # [q_len, L]
                 for t in range(q_len):
@@ -124,6 +138,8 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale: float, G: int,
                     out[b, t, h] = w @ V[:n]
                     if weights is not None:
                         weights[(b, t, h)] = w
+    if head_active is not None:
+        out[np.asarray(head_active) == 0] = 0.0
     if return_weights:
         return out, weights
     return out

@@ -239,3 +239,23 @@ def test_row_blocks_split_large_groups_evenly():
         assert st == OK and pl.row_blocks == -(-R // 256)
         assert pl.row_blocks * rb_rows >= R and rb_rows % 16 == 0
         assert pl.workspace_bytes == ro(64 * 2 * rb_rows * 128 * 4) + ro(64 * 2 * rb_rows * 4) + ro(3 * 4)
+
+
+def test_grouping_variant_checks():
+    hg = P  # a fake aligned device pointer; validation never dereferences it
+    # bf16 with a head map: any H, G with G <= H; the plan sizes rows by max_group_heads
+    st, pl = plan(H=40, G=6, q_len=2, o=opts(head_group=hg))
+    assert st == OK and pl.policy == _lib.GQA_POLICY_MFMA and pl.rows == 40 * 2
+    st, pl = plan(H=40, G=6, q_len=2, o=opts(head_group=hg, max_group_heads=10))
+    assert st == OK and pl.rows == 20
+    assert plan(H=8, G=9, o=opts(head_group=hg))[0] == INV             # G > H
+    assert plan(H=40, G=6, o=opts(head_group=hg, max_group_heads=41))[0] == INV
+    assert plan(H=40, G=6, o=opts(head_group=hg, max_group_heads=-1))[0] == INV
+    assert plan(H=40, G=6, o=opts(head_group=hg + 2))[0] == INV        # misaligned map
+    assert plan(H=300, G=6, o=opts(head_group=hg))[0] == UNS           # more than 256 heads
+    assert plan(H=8, G=2, o=opts(head_group=hg, dtype=_lib.GQA_DTYPE_F32))[0] == UNS
+    assert plan(H=8, G=2, o=opts(head_active=P, policy=_lib.GQA_POLICY_VALU))[0] == UNS
+    st, pl = plan(H=8, G=8, o=opts(head_active=P))                      # R = 1 still on MFMA
+    assert st == OK and pl.policy == _lib.GQA_POLICY_MFMA
+    assert plan(H=8, G=2, o=opts(reserved0=1))[0] == INV
+    assert plan(H=40, G=6)[0] == INV                                      # no map: H % G must be 0

@@ -488,3 +488,66 @@ def test_planted_append_position_mistake_is_caught():
                 wrong[b, :, pos] = kn[b, t]
     exp = _concatenated(ok, kn, old_lens, lens)
     assert not all(np.array_equal(wrong[b, :, :lens[b]], exp[b, :, :lens[b]]) for b in range(len(lens)))
+
+
+# ------------------------------ grouping variants: call-time head map, active mask
+
+def sdpa_gather_reference(q, k, v, lens, scale, head_group, causal=True):
+    """torch fp64 SDPA with each query head's K/V gathered by index_select through the
+    map (the non-uniform counterpart of repeat_interleave), explicit bottom-right mask."""
+    import torch
+    import torch.nn.functional as F
+    B, q_len, H, d = q.shape
+    idx = torch.as_tensor(np.asarray(head_group, dtype=np.int64))
+    out = np.empty_like(q)
+    for b in range(B):
+        L = int(lens[b])
+        qt = torch.from_numpy(q[b:b + 1]).transpose(1, 2)
+        kt = torch.from_numpy(np.ascontiguousarray(k[b:b + 1, :, :L])).index_select(1, idx)
+        vt = torch.from_numpy(np.ascontiguousarray(v[b:b + 1, :, :L])).index_select(1, idx)
+        mask = torch.ones(q_len, L, dtype=torch.bool)
+        if causal:
+            mask = mask.tril(diagonal=L - q_len)
+        o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=float(np.float32(scale)))
+        out[b] = o.transpose(1, 2).numpy()[0]
+    return out
+
+
+def test_uniform_head_map_equals_contiguous_groups():
+    rng = np.random.default_rng(91)
+    q, k, v, lens = rand_case(rng, 2, 8, 2, 16, 3, [9, 20])
+    a = O.gqa_decode(q, k, v, lens, 0.3, 2)
+    b = O.gqa_decode(q, k, v, lens, 0.3, 2, head_group=[h // 4 for h in range(8)])
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("head_group", [
+    [2, 0, 0, 1, 2, 2, 2, 0],        # unequal groups, interleaved
+    [1, 1, 1, 1, 1, 1, 1, 1],        # every head on one KV head; KV heads 0 and 2 idle
+    [0, 1, 2, 0, 1, 2, 0, 1],        # strided
+])
+def test_head_map_matches_gathered_sdpa(head_group):
+    rng = np.random.default_rng(92)
+    q, k, v, lens = rand_case(rng, 2, 8, 3, 16, 3, [9, 20])
+    ref = sdpa_gather_reference(q, k, v, lens, 0.3, head_group)
+    got = O.gqa_decode(q, k, v, lens, 0.3, 3, head_group=head_group)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_planted_head_map_ignored_is_caught():
+    rng = np.random.default_rng(93)
+    q, k, v, lens = rand_case(rng, 1, 8, 2, 8, 2, [12])
+    hg = [1, 0, 1, 0, 0, 0, 1, 1]
+    ref = sdpa_gather_reference(q, k, v, lens, 0.5, hg)
+    wrong = O.gqa_decode(q, k, v, lens, 0.5, 2)          # contiguous groups instead of the map
+    assert not np.allclose(wrong, ref, rtol=0, atol=1e-6)
+
+
+def test_inactive_pairs_are_zero_and_others_unchanged():
+    rng = np.random.default_rng(94)
+    q, k, v, lens = rand_case(rng, 2, 8, 2, 16, 3, [9, 20])
+    act = (rng.random((2, 3, 8)) < 0.5).astype(np.uint8)
+    full = O.gqa_decode(q, k, v, lens, 0.3, 2)
+    got = O.gqa_decode(q, k, v, lens, 0.3, 2, head_active=act)
+    np.testing.assert_array_equal(got[act == 0], 0.0)
+    np.testing.assert_array_equal(got[act == 1], full[act == 1])
