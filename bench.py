@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--policy", default="auto", choices=["auto", "valu", "mfma"])
+    ap.add_argument("--head-map", action="store_true",
+                    help="non-uniform grouping: a seeded head->KV-head map with groups of up to 2*H/G heads")
+    ap.add_argument("--active-frac", type=float, default=0.0,
+                    help="per-(token, head) active mask with this fraction of pairs active (0: no mask)")
     ap.add_argument("--append", action="store_true",
                     help="time gqa_decode_append: the step also writes the new tokens' K/V into the cache")
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies rotated (0: enough for >= 1 GiB)")
@@ -175,10 +179,27 @@ def main():
         ks.append(inp.k_cache.clone())
         vs.append(inp.v_cache.clone())
     out = torch.empty_like(inp.q)
+    variant = {}
+    if args.head_map:
+        # every KV head keeps at least one query head; the rest are dealt at random with
+        # at most twice the uniform group size per KV head
+        rng = np.random.default_rng(wl.seed + 7)
+        hpg = wl.H // wl.G
+        while True:
+            m = np.concatenate([np.arange(wl.G), rng.integers(0, wl.G, wl.H - wl.G)])
+            rng.shuffle(m)
+            if np.bincount(m, minlength=wl.G).max() <= 2 * hpg:
+                break
+        variant["head_group"] = torch.as_tensor(m.astype(np.int32), device=dev)
+        variant["max_group_heads"] = 2 * hpg
+    if args.active_frac > 0:
+        rng = np.random.default_rng(wl.seed + 8)
+        act = (rng.random((wl.B, wl.q_len, wl.H)) < args.active_frac).astype(np.uint8)
+        variant["head_active"] = torch.as_tensor(act, device=dev)
     kw = dict(scale=wl.scale, causal=wl.causal, num_splits=args.num_splits, chunk_tokens=args.chunk,
-              policy=args.policy)
+              policy=args.policy, **variant)
     pl = plan(inp.q, inp.k_cache, inp.block_table, causal=wl.causal, num_splits=args.num_splits,
-              chunk_tokens=args.chunk, policy=args.policy)
+              chunk_tokens=args.chunk, policy=args.policy, **variant)
     ws = torch.empty(max(pl["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
 
     new_bytes = 0
@@ -284,7 +305,8 @@ def main():
         "dtype": "bf16" if wl.dtype == "bfloat16" else "f32",
         "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and block tables)",
         "config": {
-            "workload": name + (" +append" if args.append else ""),
+            "workload": name + (" +append" if args.append else "") + (" +head_map" if args.head_map else "")
+            + (f" +active{args.active_frac:g}" if args.active_frac > 0 else ""),
             "B": wl.B, "H": wl.H, "G": wl.G, "d_h": wl.d_h, "q_len": wl.q_len,
             "layout": wl.layout, "page_size": wl.page_size or None,
             "lengths": [wl.len_lo, wl.len_hi], "sum_seq_lens": int(inp.lens.sum()),
@@ -300,7 +322,7 @@ def main():
             "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
             "unit": "TFLOP/s" if mfma_bound else "GB/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS if mfma_bound else achieved / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(name + ("_append" if args.append else "")),
+            "traffic": load_traffic(name + ("_append" if args.append else "")) if not variant else None,
             "kernel": "decode_mfma_kernel" if pl["policy"] == "mfma" else "decode_valu_kernel",
             "algorithmic_bytes_per_launch": int(dec_alg_bytes),
             "flops_per_launch": int(flops),
