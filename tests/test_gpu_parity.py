@@ -59,6 +59,10 @@ CASES = [
     (2, 30, 1, 128, 10, [900, 40], "bfloat16", 32),    # R = 300: two blocks of 160, paged 32
     (2, 64, 1, 64, 9, [300, 50], "bfloat16", 0),       # R = 576: three blocks of 192, d = 64
     (2, 32, 2, 128, 12, [700, 64], "bfloat16", 32),    # q_len 12, R = 192, paged 32
+    (1, 32, 1, 128, 16, [600], "float32", 0),          # fp32, R = 512 on the vector ALUs
+    (2, 16, 2, 64, 16, [300, 17], "float32", 32),      # fp32, q_len 16, paged 32, L ~ q_len
+    (3, 8, 8, 128, 1, [1, 2, 3], "bfloat16", 0),       # MHA, R = 1, tiny sequences
+    (2, 64, 8, 128, 1, [131, 32768], "bfloat16", 0),   # one long, one short sequence
 ]
 
 
