@@ -33,6 +33,7 @@ EXPORTED = (
     "gqa_status_string",
     "gqa_abi_version",
     "gqa_bench_read_stream",
+    "gqa_bench_read_stream_lds",
 )
 
 
@@ -126,6 +127,8 @@ def lib() -> ctypes.CDLL:
     L.gqa_abi_version.restype = i32
     L.gqa_bench_read_stream.argtypes = [vp, sz, vp, vp]
     L.gqa_bench_read_stream.restype = i32
+    L.gqa_bench_read_stream_lds.argtypes = [vp, sz, i32, vp]
+    L.gqa_bench_read_stream_lds.restype = i32
     _lib = L
     return L
 

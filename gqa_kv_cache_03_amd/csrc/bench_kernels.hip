@@ -47,7 +47,51 @@ __global__ __launch_bounds__(kThreads) void read_stream_kernel(const u32x4* __re
   if (threadIdx.x == 0) sink[blockIdx.x] = red[0];
 }
 
+// The decode kernel's own streaming pattern without its compute: two persistent
+// workgroups per CU, each reading one contiguous share of the buffer in 16 KiB steps
+// of direct-to-LDS loads (four 16-byte loads per lane), one step in flight while the
+// wave issues the next. The LDS copies are not read.
+constexpr int kStepChunks = 4;  // 16-byte loads per lane per step
+
+__device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 2);
+#else
+  (void)src;
+  (void)lds_wave_base;
+#endif
+}
+
+__global__ __launch_bounds__(kThreads) void read_stream_lds_kernel(const unsigned char* __restrict__ buf, size_t n16) {
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2][kStepChunks * kThreads * 16];
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = (size_t)blockIdx.x * per;
+  const size_t hi = lo + per < n16 ? lo + per : n16;
+  const int wave = threadIdx.x >> 6;
+  int stage = 0;
+  for (size_t base = lo; base < hi; base += (size_t)kStepChunks * kThreads) {
+#pragma unroll
+    for (int u = 0; u < kStepChunks; ++u) {
+      const size_t i = base + (size_t)u * kThreads + threadIdx.x;
+      if (i < hi) dma16(buf + i * 16, &lds[stage][u * kThreads * 16 + wave * 1024]);
+    }
+    // at most this step's loads stay in flight: vmcnt(4), expcnt and lgkmcnt untouched
+    __builtin_amdgcn_s_waitcnt((kStepChunks & 15) | (7 << 4) | (15 << 8));
+    stage ^= 1;
+  }
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+}
+
 }  // namespace
+
+extern "C" int gqa_bench_read_stream_lds(const void* buf, size_t bytes, int workgroups, void* stream) {
+  if (!buf || bytes == 0 || (bytes % 16) != 0 || workgroups <= 0 || workgroups > (1 << 20))
+    return GQA_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(buf) % 16) != 0) return GQA_ERR_INVALID_ARGUMENT;
+  hipLaunchKernelGGL(read_stream_lds_kernel, dim3(workgroups), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const unsigned char*>(buf), bytes / 16);
+  return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
 
 extern "C" int gqa_bench_read_stream(const void* buf, size_t bytes, void* sink, void* stream) {
   if (!buf || !sink || bytes == 0 || (bytes % 16) != 0) return GQA_ERR_INVALID_ARGUMENT;

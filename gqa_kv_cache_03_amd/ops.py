@@ -189,10 +189,22 @@ def workspace_bytes(q, k_cache, block_table=None, **kw) -> int:
     return plan(q, k_cache, block_table, **kw)["workspace_bytes"]
 
 
-def read_stream(buf, sink) -> None:
-    """Measurement helper: stream-read `buf` (a device tensor) once."""
+def read_stream(buf, sink=None, workgroups: int = 0) -> None:
+    """Measurement helper: stream-read `buf` (a device tensor) once.
+
+    With `sink` (int32 device tensor of >= 8192 entries): wide nontemporal loads into
+    registers. Without: the decode kernel's pattern, `workgroups` persistent workgroups
+    (0: two per CU) reading through direct-to-LDS double-buffered steps.
+    """
     import torch
-    st = _lib.lib().gqa_bench_read_stream(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
-                                          torch.cuda.current_stream(buf.device).cuda_stream)
+    L = _lib.lib()
+    stream = torch.cuda.current_stream(buf.device).cuda_stream
+    nbytes = buf.numel() * buf.element_size()
+    if sink is not None:
+        st = L.gqa_bench_read_stream(buf.data_ptr(), nbytes, sink.data_ptr(), stream)
+    else:
+        if workgroups <= 0:
+            workgroups = 2 * torch.cuda.get_device_properties(buf.device).multi_processor_count
+        st = L.gqa_bench_read_stream_lds(buf.data_ptr(), nbytes, workgroups, stream)
     if st != _lib.GQA_OK:
         raise GqaError(st, "gqa_bench_read_stream")

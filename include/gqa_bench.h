@@ -28,6 +28,15 @@ extern "C" {
  */
 int gqa_bench_read_stream(const void* buf, size_t bytes, void* sink, void* stream);
 
+/*
+ * gqa_bench_read_stream_lds -- read `bytes` bytes at `buf` (16-byte aligned, a
+ * multiple of 16) the way the decode kernel streams its cache, minus the compute:
+ * `workgroups` persistent workgroups (the decode kernel uses two per CU) each read one
+ * contiguous share in 16 KiB steps of direct-to-LDS loads, one step in flight.
+ * Asynchronous on `stream`. Returns a gqa_status.
+ */
+int gqa_bench_read_stream_lds(const void* buf, size_t bytes, int workgroups, void* stream);
+
 #pragma GCC visibility pop
 
 #ifdef __cplusplus
