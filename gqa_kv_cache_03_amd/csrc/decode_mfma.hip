@@ -18,11 +18,17 @@
 // them (flash-decoding split-K over context, with splits sized by work, not by length).
 //
 // Per workgroup: the group's R = (H/G) * q_len query rows are packed into 16-row MFMA
-// tiles held in registers. K/V rows stream from HBM exactly once (the aiwiki note
-// after the listing: the cache is read once, not copied per head) through a 4-stage
-// LDS ring filled by direct global->LDS loads (nontemporal, 16 bytes per lane); the
-// ring keeps running across segment boundaries. Every packed row consumes each staged
-// tile, i.e. the H/G-fold broadcast happens in registers, never in memory.
+// tiles held in registers (a group of more than 256 rows is split into row blocks,
+// each a segment of its own). K/V rows stream from HBM exactly once per row block (the
+// aiwiki note after the listing: the cache is read once, not copied per head) through
+// a double-buffered LDS ring filled by direct global->LDS loads (nontemporal, 16 bytes
+// per lane); the ring keeps running across segment boundaries. Every packed row
+// consumes each staged tile, i.e. the H/G-fold broadcast happens in registers, never
+// in memory.
+//
+// Options handled here as well: the cache append (the new tokens' rows come from
+// k_new / v_new and are copied into the cache from LDS), a call-time head -> KV head
+// map (non-uniform groups) and a per-(token, head) active mask.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, A 16x32 / B 32x16 / C 16x16):
 //   S^T = K Q^T with K as the A operand (rows = keys) and Q^T as B (columns = query
@@ -418,7 +424,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   // back the chunks its own loads placed) into the cache. Called right after the
   // tile's wait, while nothing else is in flight.
   auto copy_new_rows = [&](const Cursor& c, int f) {
-    if (!tile_has_new(c)) return;
+    // every row block of a group stages the same tile; the first one writes it
+    if (!tile_has_new(c) || c.rb != 0) return;
     const unsigned char* st = smem + (f % NS) * C::STAGE_BYTES;
     const int t0 = c.t * T;
     const int new0 = c.L - p.q_len;

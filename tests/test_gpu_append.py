@@ -65,6 +65,7 @@ CASES = [
     (2, 16, 16, 128, 1, [300, 1025], "bfloat16", 0),    # R = 1 -> vector-ALU path
     (2, 8, 2, 128, 2, [77, 300], "float32", 0),         # fp32 -> vector-ALU path
     (2, 4, 1, 64, 3, [40, 129], "float32", 16),         # fp32, paged
+    (1, 32, 1, 128, 16, [700], "bfloat16", 32),         # R = 512: two row blocks, paged 32
 ]
 
 
