@@ -251,13 +251,13 @@ struct MfmaCfg {
   static constexpr int TENSOR_BYTES = T * ROW_BYTES;
   static constexpr int STAGE_BYTES = 2 * TENSOR_BYTES;
   static constexpr int LOADS = T * CPR / kThreads;  // 16-B loads per thread per tensor
+  static constexpr int RPL = kThreads / CPR;        // tile rows covered by one such load
   static constexpr int LD = 2 * LOADS;              // per thread per stage (K and V)
   static constexpr int LDS_BYTES = NS * STAGE_BYTES;
   static_assert(NRW * NCW == 4, "four waves per workgroup");
   static_assert(KB == 2, "one 32-deep PV product per tile");
   static_assert(LOADS >= 1 && (T * CPR) % kThreads == 0, "stage load split");
   static_assert(CB % NCW == 0, "column split");
-  static_assert(LDS_BYTES >= (kThreads + 8) * 4, "start-up scratch fits in the ring");
 };
 
 // Position in the flattened tile sequence: segment (b, g, rb) -- row block rb of KV
@@ -390,12 +390,42 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     }
   };
 
+  // Lane-constant part of a staging load: load n of this lane covers tile row
+  // n * RPL + rl, 16-byte chunk pch, and fetches global chunk pch ^ swizzle(row). The
+  // swizzles depend on the row modulo CPR, and RPL is a multiple of CPR, so the
+  // offsets within a row block are the same for every n.
+  const int rl = tid / CPR;
+  const int pch = tid % CPR;
+  const uint32_t koff = (uint32_t)(rl * ROW_BYTES + ((pch ^ swz_k<CPR>(rl)) << 4));
+  const uint32_t voff = (uint32_t)(rl * ROW_BYTES + ((pch ^ swz_v<CPR>(rl)) << 4));
+  static_assert(C::RPL % CPR == 0, "swizzle period divides the rows per load");
+
   auto issue_tile = [&](const Cursor& c, int f) {
     unsigned char* st = smem + (f % NS) * C::STAGE_BYTES;
     const int t0 = c.t * T;
     const int end = c.L;
     const int new0 = end - p.q_len;
     const bool has_new = tile_has_new(c);
+    // A full tile (no row past the end, no new token) whose loads each stay within one
+    // page: a scalar base per load plus the lane-constant offsets.
+    if (t0 + T <= end && !has_new && (!PAGED || (1 << pshift) >= C::RPL)) {
+#pragma unroll
+      for (int n = 0; n < LOADS; ++n) {
+        const int j0 = t0 + n * C::RPL;  // first row of this load
+        size_t rb;
+        if constexpr (PAGED) {
+          int page = load_uniform_i32(p.table + (size_t)c.b * p.max_blocks, j0 >> pshift);
+          page = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
+          rb = (((size_t)page * p.G + c.g) * (size_t)(pmask + 1) + (j0 & pmask)) * ROW_BYTES;
+        } else {
+          rb = (((size_t)c.b * p.G + c.g) * (size_t)p.capacity + j0) * ROW_BYTES;
+        }
+        const int lds_off = n * kThreads * 16 + wave * 1024;  // this wave's 64 x 16 B slots
+        load16_to_lds(kg + rb + koff, st + lds_off);
+        load16_to_lds(vg + rb + voff, st + C::TENSOR_BYTES + lds_off);
+      }
+      return;
+    }
     int pg[T / 16] = {};
     tile_pages(c, pg);
 #pragma unroll
