@@ -94,7 +94,8 @@ def calibrate_copy(mib: int) -> None:
 
 def cpu_baseline(inp, budget_s: float):
     """Time the oracle, as it is, on (sequence, KV group) units in order until the
-    budget is spent; report KV GB/s over the sample."""
+    budget is spent -- starting over from the first unit when a pass over the whole
+    workload ends sooner -- and report KV GB/s over the sample."""
     import numpy as np
     import oracle
     try:
@@ -103,33 +104,46 @@ def cpu_baseline(inp, budget_s: float):
         threadpool_info = lambda: []
     wl = inp.wl
     hpg = wl.H // wl.G
-    done_bytes, elapsed, units = 0, 0.0, 0
-    for b in range(wl.B):
+    n_units = wl.B * wl.G
+    # host fp32 copies are made outside the timer; kept across passes when they fit
+    keep = 2 * 4 * wl.d_h * int(sum(int(L) for L in inp.lens)) * wl.G <= (4 << 30)
+    cache = {}
+
+    def unit(b, g):
+        if (b, g) in cache:
+            return cache[(b, g)]
         L = int(inp.lens[b])
-        for g in range(wl.G):
-            q = inp.q[b:b + 1, :, g * hpg:(g + 1) * hpg].float().cpu().numpy()
-            if inp.block_table is None:
-                k = inp.k_cache[b:b + 1, g:g + 1, :L].float().cpu().numpy()
-                v = inp.v_cache[b:b + 1, g:g + 1, :L].float().cpu().numpy()
-                tbl, P = None, 0
-            else:
-                import torch
-                P = wl.page_size
-                n = -(-L // P)
-                pages = torch.as_tensor(inp.table[b, :n].astype(np.int64), device=inp.k_cache.device)
-                k = inp.k_cache[pages][:, g:g + 1].float().cpu().numpy()
-                v = inp.v_cache[pages][:, g:g + 1].float().cpu().numpy()
-                tbl = np.arange(n, dtype=np.int64)[None, :]
+        q = inp.q[b:b + 1, :, g * hpg:(g + 1) * hpg].float().cpu().numpy()
+        if inp.block_table is None:
+            k = inp.k_cache[b:b + 1, g:g + 1, :L].float().cpu().numpy()
+            v = inp.v_cache[b:b + 1, g:g + 1, :L].float().cpu().numpy()
+            tbl, P = None, 0
+        else:
+            import torch
+            P = wl.page_size
+            n = -(-L // P)
+            pages = torch.as_tensor(inp.table[b, :n].astype(np.int64), device=inp.k_cache.device)
+            k = inp.k_cache[pages][:, g:g + 1].float().cpu().numpy()
+            v = inp.v_cache[pages][:, g:g + 1].float().cpu().numpy()
+            tbl = np.arange(n, dtype=np.int64)[None, :]
+        args = (q, k, v, tbl, P)
+        if keep:
+            cache[(b, g)] = args
+        return args
+
+    done_bytes, elapsed, units = 0, 0.0, 0
+    while units == 0 or elapsed < budget_s:
+        for i in range(n_units):
+            b, g = divmod(i, wl.G)
+            q, k, v, tbl, P = unit(b, g)
             t0 = time.perf_counter()
             oracle.gqa_decode(q, k, v, inp.lens[b:b + 1], wl.scale, 1, block_table=tbl, page_size=P,
                               causal=wl.causal)
             elapsed += time.perf_counter() - t0
-            done_bytes += 2 * wl.d_h * wl.itemsize * L
+            done_bytes += 2 * wl.d_h * wl.itemsize * int(inp.lens[b])
             units += 1
             if elapsed >= budget_s:
                 break
-        if elapsed >= budget_s:
-            break
     threads = 0
     for info in threadpool_info():
         if info.get("user_api") == "blas":
@@ -143,10 +157,11 @@ def cpu_baseline(inp, budget_s: float):
         "unit": "GB/s",
         "cores": threads or avail,
         "kind": "oracle",
-        "sample": (f"{units} of {wl.B * wl.G} (sequence, KV group) units, {elapsed:.1f} s of fp64 numpy "
-                   f"oracle time; {done_bytes / 1e6:.1f} MB of KV; host fp32 copies of the inputs, "
-                   f"upcast inside the timed region; {avail} cores visible"),
-        "tokens_per_s_equiv": round(units / (wl.B * wl.G) * wl.B * wl.q_len / elapsed, 3),
+        "sample": (f"{units} (sequence, KV group) units in order ({units / n_units:.2f} passes over the "
+                   f"workload's {n_units}), {elapsed:.1f} s of fp64 numpy oracle time; "
+                   f"{done_bytes / 1e6:.1f} MB of KV; host fp32 copies of the inputs, upcast inside the "
+                   f"timed region; {avail} cores visible"),
+        "tokens_per_s_equiv": round(units / n_units * wl.B * wl.q_len / elapsed, 3),
     }
 
 
@@ -243,7 +258,8 @@ def main():
     print(f"[bench] {args.steps} steps: {ms * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us)",
           file=sys.stderr, flush=True)
 
-    # per-kernel durations: events recorded by the library around each launch
+    # per-kernel durations: the library's launches stamp these events with each kernel's own
+    # begin and end times, so they time the kernels alone, as a kernel trace does
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for trio in evs:
         for ev in trio:
@@ -279,6 +295,9 @@ def main():
             fn()
             torch.cuda.synchronize()
             c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            # one launch ahead of the first event keeps the device busy while the host
+            # queues the rest, so the host's launch latency stays out of the timing
+            fn()
             c0.record()
             for _ in range(10):
                 fn()

@@ -264,26 +264,27 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const void*
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(opts->profile_events));
-  if (ev[0] && hipEventRecord(ev[0], s) != hipSuccess) return GQA_ERR_HIP;
   const dim3 grid(pl.grid[0], pl.grid[1], pl.grid[2]);
   if (k_new && pl.policy != GQA_POLICY_MFMA) {
     // the vector-ALU kernel reads every key from the cache: write the new rows first
     if (gqa::launch_append(dp, opts->dtype == GQA_DTYPE_BF16 ? 2 : 4, d_h, p.paged, s) != hipSuccess)
       return GQA_ERR_HIP;
   }
+  // the profile events ride on the launches: [0]/[1] take the decode kernel's own begin
+  // and end times, [2] the merge kernel's end
   hipError_t e = (pl.policy == GQA_POLICY_MFMA)
-                     ? gqa::launch_decode_mfma(dp, opts->dtype, d_h, p.paged, grid, s)
-                     : gqa::launch_decode_valu(dp, opts->dtype, d_h, p.paged, grid, s);
+                     ? gqa::launch_decode_mfma(dp, opts->dtype, d_h, p.paged, grid, s, ev[0], ev[1])
+                     : gqa::launch_decode_valu(dp, opts->dtype, d_h, p.paged, grid, s, ev[0], ev[1]);
   if (e != hipSuccess) return GQA_ERR_HIP;
-  if (ev[1] && hipEventRecord(ev[1], s) != hipSuccess) return GQA_ERR_HIP;
   if (pl.policy == GQA_POLICY_MFMA) {
-    e = gqa::launch_merge_persistent(dp, d_h, s);
+    e = gqa::launch_merge_persistent(dp, d_h, s, nullptr, ev[2]);
     if (e != hipSuccess) return GQA_ERR_HIP;
   } else if (pl.max_splits > 1) {
-    e = gqa::launch_merge(dp, opts->dtype, d_h, s);
+    e = gqa::launch_merge(dp, opts->dtype, d_h, s, nullptr, ev[2]);
     if (e != hipSuccess) return GQA_ERR_HIP;
+  } else if (ev[2] && hipEventRecord(ev[2], s) != hipSuccess) {
+    return GQA_ERR_HIP;
   }
-  if (ev[2] && hipEventRecord(ev[2], s) != hipSuccess) return GQA_ERR_HIP;
   return GQA_OK;
 }
 

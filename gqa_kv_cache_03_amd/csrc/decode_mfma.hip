@@ -803,11 +803,14 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 }
 
 template <int D, int NRW, int NCW, int RTW>
-hipError_t launch_variant(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream) {
+hipError_t launch_variant(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream, hipEvent_t start,
+                          hipEvent_t stop) {
   if (paged)
-    hipLaunchKernelGGL((decode_mfma_kernel<D, NRW, NCW, RTW, true>), grid, dim3(kThreads), 0, stream, p);
+    hipExtLaunchKernelGGL((decode_mfma_kernel<D, NRW, NCW, RTW, true>), grid, dim3(kThreads), 0, stream, start, stop,
+                          0, p);
   else
-    hipLaunchKernelGGL((decode_mfma_kernel<D, NRW, NCW, RTW, false>), grid, dim3(kThreads), 0, stream, p);
+    hipExtLaunchKernelGGL((decode_mfma_kernel<D, NRW, NCW, RTW, false>), grid, dim3(kThreads), 0, stream, start,
+                          stop, 0, p);
   return hipGetLastError();
 }
 
@@ -830,9 +833,10 @@ int variant_occupancy(bool paged) {
   X(256, 4, 1, 4)
 
 template <int D>
-hipError_t launch_for_rows(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream) {
+hipError_t launch_for_rows(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream, hipEvent_t start,
+                           hipEvent_t stop) {
 #define X(ROWS, NRW, NCW, RTW) \
-  if (p.row_block <= ROWS) return launch_variant<D, NRW, NCW, RTW>(p, paged, grid, stream);
+  if (p.row_block <= ROWS) return launch_variant<D, NRW, NCW, RTW>(p, paged, grid, stream, start, stop);
   GQA_MFMA_VARIANTS(X)
 #undef X
   return hipErrorInvalidValue;
@@ -856,10 +860,10 @@ MfmaVariant mfma_variant_for_rows(int R, int d_h, bool paged, bool query_device)
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int d_h, bool paged, dim3 grid,
-                              hipStream_t stream) {
+                              hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   (void)dtype;  // bf16 only (checked by the planner)
-  if (d_h == 64) return launch_for_rows<64>(p, paged, grid, stream);
-  return launch_for_rows<128>(p, paged, grid, stream);
+  if (d_h == 64) return launch_for_rows<64>(p, paged, grid, stream, start, stop);
+  return launch_for_rows<128>(p, paged, grid, stream, start, stop);
 }
 
 }  // namespace gqa

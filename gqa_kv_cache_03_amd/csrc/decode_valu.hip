@@ -200,21 +200,24 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeParams p) {
 }
 
 template <typename TT, int D, int RB>
-hipError_t launch3(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream) {
+hipError_t launch3(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream, hipEvent_t start,
+                   hipEvent_t stop) {
   if (paged)
-    hipLaunchKernelGGL((decode_valu_kernel<TT, D, RB, true>), grid, dim3(kThreads), 0, stream, p);
+    hipExtLaunchKernelGGL((decode_valu_kernel<TT, D, RB, true>), grid, dim3(kThreads), 0, stream, start, stop, 0, p);
   else
-    hipLaunchKernelGGL((decode_valu_kernel<TT, D, RB, false>), grid, dim3(kThreads), 0, stream, p);
+    hipExtLaunchKernelGGL((decode_valu_kernel<TT, D, RB, false>), grid, dim3(kThreads), 0, stream, start, stop, 0,
+                          p);
   return hipGetLastError();
 }
 
 template <typename TT, int D>
-hipError_t launch2(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream) {
+hipError_t launch2(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream, hipEvent_t start,
+                   hipEvent_t stop) {
   switch (p.row_block) {
-    case 1: return launch3<TT, D, 1>(p, paged, grid, stream);
-    case 2: return launch3<TT, D, 2>(p, paged, grid, stream);
-    case 4: return launch3<TT, D, 4>(p, paged, grid, stream);
-    default: return launch3<TT, D, 8>(p, paged, grid, stream);
+    case 1: return launch3<TT, D, 1>(p, paged, grid, stream, start, stop);
+    case 2: return launch3<TT, D, 2>(p, paged, grid, stream, start, stop);
+    case 4: return launch3<TT, D, 4>(p, paged, grid, stream, start, stop);
+    default: return launch3<TT, D, 8>(p, paged, grid, stream, start, stop);
   }
 }
 
@@ -232,13 +235,13 @@ int valu_lds_bytes(int dtype, int d_h, int row_block) {
 }
 
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int d_h, bool paged, dim3 grid,
-                              hipStream_t stream) {
+                              hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if (dtype == 0) {
-    if (d_h == 64) return launch2<float, 64>(p, paged, grid, stream);
-    return launch2<float, 128>(p, paged, grid, stream);
+    if (d_h == 64) return launch2<float, 64>(p, paged, grid, stream, start, stop);
+    return launch2<float, 128>(p, paged, grid, stream, start, stop);
   }
-  if (d_h == 64) return launch2<__bf16, 64>(p, paged, grid, stream);
-  return launch2<__bf16, 128>(p, paged, grid, stream);
+  if (d_h == 64) return launch2<__bf16, 64>(p, paged, grid, stream, start, stop);
+  return launch2<__bf16, 128>(p, paged, grid, stream, start, stop);
 }
 
 }  // namespace gqa

@@ -1,6 +1,7 @@
 // Internal declarations shared by the host planner and the kernel translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -43,12 +44,17 @@ struct DecodeParams {
 // Row r of the packed group tile is query token t = r / hpg of head g*hpg + r % hpg.
 
 // Launchers (defined next to their kernels). Return hipSuccess or the launch error.
+// `start` / `stop` (may be null) are caller-created events that the launch itself
+// stamps with the kernel's own begin and end times (hipExtLaunchKernel), so the
+// elapsed time between them is that kernel's execution, free of queue gaps.
 hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int d_h, bool paged,
-                              dim3 grid, hipStream_t stream);
+                              dim3 grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_decode_valu(const DecodeParams& p, int dtype, int d_h, bool paged,
-                              dim3 grid, hipStream_t stream);
-hipError_t launch_merge(const DecodeParams& p, int dtype, int d_h, hipStream_t stream);
-hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t stream);
+                              dim3 grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+hipError_t launch_merge(const DecodeParams& p, int dtype, int d_h, hipStream_t stream, hipEvent_t start,
+                        hipEvent_t stop);
+hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t stream, hipEvent_t start,
+                                   hipEvent_t stop);
 // Writes k_new / v_new into the cache rows of the new tokens (vector-ALU path).
 hipError_t launch_append(const DecodeParams& p, int elem_bytes, int d_h, bool paged, hipStream_t stream);
 

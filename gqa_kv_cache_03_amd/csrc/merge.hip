@@ -120,9 +120,9 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
 }
 
 template <typename TT, int D>
-hipError_t go(const DecodeParams& p, hipStream_t stream) {
+hipError_t go(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const int total = p.B * p.q_len * p.H;
-  hipLaunchKernelGGL((merge_kernel<TT, D>), dim3(total), dim3(kThreads), 0, stream, p);
+  hipExtLaunchKernelGGL((merge_kernel<TT, D>), dim3(total), dim3(kThreads), 0, stream, start, stop, 0, p);
   return hipGetLastError();
 }
 
@@ -259,21 +259,23 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
 }
 
 template <int D>
-hipError_t go_persistent(const DecodeParams& p, hipStream_t stream) {
+hipError_t go_persistent(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 grid(p.B * p.G * p.n_row_blocks * p.row_block);
-  hipLaunchKernelGGL((merge_persistent_kernel<D>), grid, dim3(kThreads), 0, stream, p);
+  hipExtLaunchKernelGGL((merge_persistent_kernel<D>), grid, dim3(kThreads), 0, stream, start, stop, 0, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t stream) {
-  return d_h == 64 ? go_persistent<64>(p, stream) : go_persistent<128>(p, stream);
+hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t stream, hipEvent_t start,
+                                   hipEvent_t stop) {
+  return d_h == 64 ? go_persistent<64>(p, stream, start, stop) : go_persistent<128>(p, stream, start, stop);
 }
 
-hipError_t launch_merge(const DecodeParams& p, int dtype, int d_h, hipStream_t stream) {
-  if (dtype == 0) return d_h == 64 ? go<float, 64>(p, stream) : go<float, 128>(p, stream);
-  return d_h == 64 ? go<__bf16, 64>(p, stream) : go<__bf16, 128>(p, stream);
+hipError_t launch_merge(const DecodeParams& p, int dtype, int d_h, hipStream_t stream, hipEvent_t start,
+                        hipEvent_t stop) {
+  if (dtype == 0) return d_h == 64 ? go<float, 64>(p, stream, start, stop) : go<float, 128>(p, stream, start, stop);
+  return d_h == 64 ? go<__bf16, 64>(p, stream, start, stop) : go<__bf16, 128>(p, stream, start, stop);
 }
 
 }  // namespace gqa

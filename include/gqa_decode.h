@@ -74,8 +74,13 @@ typedef struct gqa_decode_opts {
   int32_t  policy;            /* gqa_policy */
   void*    workspace;         /* device scratch for split partials (caller-owned) */
   size_t   workspace_bytes;
-  void*    profile_events[3]; /* optional hipEvent_t: recorded on `stream` before the
-                                 decode kernel, between it and the merge, after the merge */
+  void*    profile_events[3]; /* optional hipEvent_t, created by the caller with timing
+                                 on. The launches stamp them (hipExtLaunchKernel): [0] and
+                                 [1] with the decode kernel's own begin and end times, so
+                                 their elapsed time is that kernel's execution alone; [2]
+                                 with the end of the merge kernel (recorded on `stream`
+                                 after the decode kernel when no merge runs). Any may be
+                                 NULL. */
   /* Grouping variants (matrix-core policy, bf16, H <= 256; NULL/0 = plain GQA):
    *  head_group   device int32 [H]: the KV head (in [0, G)) each query head reads, for
    *               a non-uniform allocation of query heads to KV heads decided at call
