@@ -1,4 +1,4 @@
-"""CPU oracle for GQA decode. TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for GQA decode and the GQLA latent path. TEST INFRASTRUCTURE ONLY.
 
 Only the tests, the smoke entry point and the benchmark's CPU-baseline leg may
 import this package. The product path (the HIP library and its Python binding)
@@ -14,4 +14,10 @@ from .gqa_oracle import (  # noqa: F401
     append_kv,
     kv_bytes,
     touched_kv_rows,
+)
+from .gqla_oracle import (  # noqa: F401
+    latent_rows,
+    expand_cache,
+    gqla_decode,
+    latent_bytes,
 )
