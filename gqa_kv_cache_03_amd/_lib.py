@@ -34,6 +34,9 @@ EXPORTED = (
     "gqa_abi_version",
     "gqa_bench_read_stream",
     "gqa_bench_read_stream_lds",
+    "gqla_absorb_decode",
+    "gqla_absorb_plan",
+    "gqla_absorb_workspace_size",
 )
 
 
@@ -129,6 +132,14 @@ def lib() -> ctypes.CDLL:
     L.gqa_bench_read_stream.restype = i32
     L.gqa_bench_read_stream_lds.argtypes = [vp, sz, i32, vp]
     L.gqa_bench_read_stream_lds.restype = i32
+    L.gqla_absorb_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_float,
+                                     vp, ctypes.POINTER(DecodeOpts)]
+    L.gqla_absorb_decode.restype = i32
+    L.gqla_absorb_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(DecodeOpts), ctypes.POINTER(Plan)]
+    L.gqla_absorb_plan.restype = i32
+    L.gqla_absorb_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(DecodeOpts),
+                                             ctypes.POINTER(sz)]
+    L.gqla_absorb_workspace_size.restype = i32
     _lib = L
     return L
 

@@ -11,6 +11,7 @@
 #include <cstring>
 
 #include "../../include/gqa_decode.h"
+#include "../../include/gqla_absorb.h"
 #include "gqa_internal.h"
 
 namespace {
@@ -18,7 +19,7 @@ namespace {
 using gqa::DecodeParams;
 
 constexpr int kMaxRows = 1024;        // packed rows per KV group (H/G * q_len)
-constexpr int kMfmaBlockRows = 256;   // packed rows one MFMA workgroup holds
+constexpr int kLatentWidth = 512;     // d_c of the GQLA latent (the kernel's head width)
 constexpr int kMaxMappedHeads = 256;  // query heads a head -> group map may cover
 constexpr int kTargetSlots = 8192;   // split-kernel workgroup slots the VALU heuristic aims for
 constexpr size_t kWsAlign = 256;
@@ -59,8 +60,10 @@ struct Plan {
   size_t ws_lse_bytes;
 };
 
+// latent: the attention of the GQLA absorbed path -- one KV head (G = 1) of width
+// d_h = 512 that is both K and V, on the matrix cores only.
 int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* opts, bool paged,
-              bool query_device, Plan* out) {
+              bool query_device, Plan* out, bool latent = false) {
   if (!opts || opts->struct_size < sizeof(gqa_decode_opts)) return GQA_ERR_INVALID_ARGUMENT;
   if (B <= 0 || H <= 0 || G <= 0 || d_h <= 0 || q_len <= 0) return GQA_ERR_INVALID_ARGUMENT;
   // grouping variants: a call-time head -> KV head map and a per-(token, head) active
@@ -74,7 +77,9 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
   if (opts->dtype != GQA_DTYPE_F32 && opts->dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
   if (variant && (opts->dtype != GQA_DTYPE_BF16 || opts->policy == GQA_POLICY_VALU || H > kMaxMappedHeads))
     return GQA_ERR_UNSUPPORTED;
-  if (d_h != 64 && d_h != 128) return GQA_ERR_UNSUPPORTED;
+  if (latent ? d_h != kLatentWidth : (d_h != 64 && d_h != 128)) return GQA_ERR_UNSUPPORTED;
+  if (latent && (variant || opts->dtype != GQA_DTYPE_BF16 || opts->policy == GQA_POLICY_VALU))
+    return GQA_ERR_UNSUPPORTED;
   if (opts->causal != 0 && opts->causal != 1) return GQA_ERR_INVALID_ARGUMENT;
   if (opts->num_splits < 0 || opts->chunk_tokens < 0) return GQA_ERR_INVALID_ARGUMENT;
   if (opts->policy < GQA_POLICY_AUTO || opts->policy > GQA_POLICY_MFMA) return GQA_ERR_INVALID_ARGUMENT;
@@ -105,7 +110,7 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
 
   int policy = opts->policy;
   if (policy == GQA_POLICY_AUTO)
-    policy = (opts->dtype == GQA_DTYPE_BF16 && (R >= 4 || variant)) ? GQA_POLICY_MFMA : GQA_POLICY_VALU;
+    policy = (opts->dtype == GQA_DTYPE_BF16 && (R >= 4 || variant || latent)) ? GQA_POLICY_MFMA : GQA_POLICY_VALU;
   if (policy == GQA_POLICY_MFMA && opts->dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
 
   gqa_plan& pub = p.pub;
@@ -121,7 +126,8 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
     // with more packed rows than one workgroup holds is split into equal row blocks,
     // each a segment that reads the group's K/V (at that size the step is bound by the
     // matrix cores, not by the extra reads).
-    const int n_rb = (int)((R + kMfmaBlockRows - 1) / kMfmaBlockRows);
+    const int block_rows = gqa::mfma_max_rows(d_h);
+    const int n_rb = (int)((R + block_rows - 1) / block_rows);
     const int rb_rows = n_rb == 1 ? (int)R : (int)(((R + n_rb - 1) / n_rb + 15) / 16 * 16);
     const long long max_tiles = (long long)B * G * n_rb * ((capacity + kMfmaTile - 1) / kMfmaTile);
     if (max_tiles > INT32_MAX / 2) return GQA_ERR_UNSUPPORTED;
@@ -202,6 +208,38 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
   return GQA_OK;
 }
 
+// Sizes, schedule and scale of a planned launch (pointers are set by the caller).
+void fill_params(DecodeParams& dp, const Plan& p, const gqa_decode_opts* opts, int B, int H, int G, int q_len,
+                 float scale) {
+  const gqa_plan& pl = p.pub;
+  dp.B = B;
+  dp.H = H;
+  dp.G = G;
+  dp.q_len = q_len;
+  dp.hpg = H / G;
+  dp.R = pl.rows;
+  dp.capacity = pl.capacity;
+  dp.page_shift = p.paged ? p.page_shift : 0;
+  dp.max_blocks = p.paged ? opts->max_blocks_per_seq : 0;
+  dp.num_pages = p.paged ? opts->num_pages : 0;
+  dp.chunk = pl.chunk_tokens;
+  dp.max_splits = pl.max_splits;
+  dp.causal = opts->causal;
+  dp.row_block = p.row_block;
+  dp.n_row_blocks = pl.row_blocks;
+  dp.nwg = pl.workgroups;
+  dp.qk_scale_log2 = scale * 1.4426950408889634f;
+}
+
+// Split partials at the start of `ws`: ws_o, then ws_lse, then the persistent
+// schedule's per-sequence prefix sums.
+void set_workspace(DecodeParams& dp, const Plan& p, void* ws_base) {
+  unsigned char* ws = static_cast<unsigned char*>(ws_base);
+  dp.ws_o = reinterpret_cast<float*>(ws);
+  dp.ws_lse = reinterpret_cast<float*>(ws + p.ws_o_bytes);
+  dp.ws_prefix = reinterpret_cast<int32_t*>(ws + p.ws_o_bytes + p.ws_lse_bytes);
+}
+
 // Shared by gqa_decode (k_new == v_new == nullptr) and gqa_decode_append.
 int decode_impl(const void* q, const void* k_new, const void* v_new, const void* k_cache,
                 const void* v_cache, const int32_t* seq_lens, const int32_t* block_table, void* out,
@@ -228,6 +266,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const void*
   }
 
   DecodeParams dp{};
+  fill_params(dp, p, opts, B, H, G, q_len, scale);
   dp.q = q;
   dp.k = k_cache;
   dp.v = v_cache;
@@ -236,31 +275,10 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const void*
   dp.seq_lens = seq_lens;
   dp.table = block_table;
   dp.out = out;
-  if (pl.workspace_bytes > 0) {
-    unsigned char* ws = static_cast<unsigned char*>(opts->workspace);
-    dp.ws_o = reinterpret_cast<float*>(ws);
-    dp.ws_lse = reinterpret_cast<float*>(ws + p.ws_o_bytes);
-    dp.ws_prefix = reinterpret_cast<int32_t*>(ws + p.ws_o_bytes + p.ws_lse_bytes);
-  }
-  dp.B = B;
-  dp.H = H;
-  dp.G = G;
-  dp.q_len = q_len;
+  if (pl.workspace_bytes > 0) set_workspace(dp, p, opts->workspace);
   dp.hpg = opts->head_group ? 1 : H / G;  // unused with a head map (groups are counted)
   dp.head_group = opts->head_group;
   dp.head_active = opts->head_active;
-  dp.R = pl.rows;
-  dp.capacity = pl.capacity;
-  dp.page_shift = p.paged ? p.page_shift : 0;
-  dp.max_blocks = p.paged ? opts->max_blocks_per_seq : 0;
-  dp.num_pages = p.paged ? opts->num_pages : 0;
-  dp.chunk = pl.chunk_tokens;
-  dp.max_splits = pl.max_splits;
-  dp.causal = opts->causal;
-  dp.row_block = p.row_block;
-  dp.n_row_blocks = pl.row_blocks;
-  dp.nwg = pl.workgroups;
-  dp.qk_scale_log2 = scale * 1.4426950408889634f;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(opts->profile_events));
@@ -285,6 +303,93 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const void*
   } else if (ev[2] && hipEventRecord(ev[2], s) != hipSuccess) {
     return GQA_ERR_HIP;
   }
+  return GQA_OK;
+}
+
+// ---- GQLA, absorbed execution ----
+
+struct LatentPlan {
+  Plan attn;           // the latent attention: G = 1, head width d_c, rows H * q_len
+  size_t q_lat_bytes;  // absorbed queries, bf16 [B q_len H, d_c]
+  size_t u_bytes;      // weighted latents, fp32 [B q_len H, d_c]
+  size_t total;        // the whole workspace: q_lat, u, then the attention's partials
+};
+
+int make_latent_plan(int B, int H, int G, int d_h, int d_c, int q_len, const gqa_decode_opts* opts,
+                     bool paged, bool query_device, LatentPlan* out) {
+  if (!opts || opts->struct_size < sizeof(gqa_decode_opts)) return GQA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || H <= 0 || G <= 0 || d_h <= 0 || d_c <= 0 || q_len <= 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (G > H || H % G != 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (opts->dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
+  if ((d_h != 64 && d_h != 128) || d_c != kLatentWidth) return GQA_ERR_UNSUPPORTED;
+  LatentPlan lp{};
+  const int st = make_plan(B, H, 1, d_c, q_len, opts, paged, query_device, &lp.attn, /*latent=*/true);
+  if (st != GQA_OK) return st;
+  const size_t rows = (size_t)B * q_len * H;
+  lp.q_lat_bytes = round_up(rows * d_c * 2, kWsAlign);
+  lp.u_bytes = round_up(rows * d_c * sizeof(float), kWsAlign);
+  lp.total = lp.q_lat_bytes + lp.u_bytes + lp.attn.pub.workspace_bytes;
+  *out = lp;
+  return GQA_OK;
+}
+
+int latent_impl(const void* q, const void* latent, const void* w_uk, const void* w_uv, const int32_t* seq_lens,
+                const int32_t* block_table, void* out, int B, int H, int G, int d_h, int d_c, int q_len,
+                float scale, void* stream, const gqa_decode_opts* opts) {
+  if (!q || !latent || !w_uk || !w_uv || !seq_lens || !out || !opts) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned(q, 16) || !aligned(latent, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16) ||
+      !aligned(out, 16) || !aligned(seq_lens, 4) || (block_table && !aligned(block_table, 4)))
+    return GQA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+  if (opts->struct_size >= sizeof(gqa_decode_opts) && !block_table && opts->page_size != 0)
+    return GQA_ERR_INVALID_ARGUMENT;
+  const bool paged = block_table != nullptr;
+  LatentPlan lp;
+  int st = make_latent_plan(B, H, G, d_h, d_c, q_len, opts, paged, /*query_device=*/false, &lp);
+  if (st != GQA_OK) return st;
+  st = make_latent_plan(B, H, G, d_h, d_c, q_len, opts, paged, /*query_device=*/true, &lp);
+  if (st != GQA_OK) return st;
+  if (!opts->workspace || !aligned(opts->workspace, kWsAlign) || opts->workspace_bytes < lp.total)
+    return GQA_ERR_WORKSPACE;
+  unsigned char* ws = static_cast<unsigned char*>(opts->workspace);
+
+  gqa::LatentProjParams pp{};
+  pp.q = q;
+  pp.w_uk = w_uk;
+  pp.w_uv = w_uv;
+  pp.q_lat = ws;
+  pp.u = reinterpret_cast<const float*>(ws + lp.q_lat_bytes);
+  pp.out = out;
+  pp.B = B;
+  pp.H = H;
+  pp.G = G;
+  pp.q_len = q_len;
+  pp.d_h = d_h;
+  pp.d_c = d_c;
+
+  // the attention over the latent: every query head (rows H * q_len) reads the one
+  // latent head, as K and as V, and leaves its weighted latent u in fp32
+  const Plan& p = lp.attn;
+  const gqa_plan& pl = p.pub;
+  DecodeParams dp{};
+  fill_params(dp, p, opts, B, H, 1, q_len, scale);
+  dp.q = pp.q_lat;
+  dp.k = latent;
+  dp.v = latent;
+  dp.seq_lens = seq_lens;
+  dp.table = block_table;
+  dp.out = ws + lp.q_lat_bytes;
+  dp.out_f32 = 1;
+  set_workspace(dp, p, ws + lp.q_lat_bytes + lp.u_bytes);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(opts->profile_events));
+  if (gqa::launch_latent_absorb_q(pp, s) != hipSuccess) return GQA_ERR_HIP;
+  const dim3 grid(pl.grid[0], pl.grid[1], pl.grid[2]);
+  if (gqa::launch_decode_mfma(dp, GQA_DTYPE_BF16, d_c, paged, grid, s, ev[0], ev[1]) != hipSuccess)
+    return GQA_ERR_HIP;
+  if (gqa::launch_merge_persistent(dp, d_c, s, nullptr, ev[2]) != hipSuccess) return GQA_ERR_HIP;
+  if (gqa::launch_latent_up_proj(pp, s) != hipSuccess) return GQA_ERR_HIP;
   return GQA_OK;
 }
 
@@ -352,6 +457,37 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
   if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return GQA_ERR_INVALID_ARGUMENT;
   return decode_impl(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table, out, B, H, G, d_h, q_len,
                      scale, stream, opts);
+}
+
+int gqla_absorb_plan(int B, int H, int G, int d_h, int d_c, int q_len, const gqa_decode_opts* opts,
+                     gqa_plan* plan) {
+  if (!plan || !opts) return GQA_ERR_INVALID_ARGUMENT;
+  const bool paged = opts->struct_size >= sizeof(gqa_decode_opts) && opts->page_size > 0;
+  LatentPlan lp;
+  int st = make_latent_plan(B, H, G, d_h, d_c, q_len, opts, paged, /*query_device=*/false, &lp);
+  if (st != GQA_OK) return st;
+  st = make_latent_plan(B, H, G, d_h, d_c, q_len, opts, paged, /*query_device=*/true, &lp);
+  if (st != GQA_OK) return st;
+  *plan = lp.attn.pub;
+  plan->workspace_bytes = lp.total;
+  return GQA_OK;
+}
+
+int gqla_absorb_workspace_size(int B, int H, int G, int d_h, int d_c, int q_len, const gqa_decode_opts* opts,
+                               size_t* bytes) {
+  if (!bytes) return GQA_ERR_INVALID_ARGUMENT;
+  gqa_plan plan;
+  const int st = gqla_absorb_plan(B, H, G, d_h, d_c, q_len, opts, &plan);
+  if (st != GQA_OK) return st;
+  *bytes = plan.workspace_bytes;
+  return GQA_OK;
+}
+
+int gqla_absorb_decode(const void* q, const void* latent_cache, const void* w_uk, const void* w_uv,
+                       const int32_t* seq_lens, const int32_t* block_table, void* out, int B, int H, int G,
+                       int d_h, int d_c, int q_len, float scale, void* stream, const gqa_decode_opts* opts) {
+  return latent_impl(q, latent_cache, w_uk, w_uv, seq_lens, block_table, out, B, H, G, d_h, d_c, q_len, scale,
+                     stream, opts);
 }
 
 }  // extern "C"

@@ -138,10 +138,21 @@ __device__ __forceinline__ void wait_tiles(int after) {
 // LDS swizzles (16-byte chunk index XOR a function of the row) so that the QK
 // A-operand reads (16 consecutive key rows, one chunk each) and the transposed V
 // reads (16 consecutive key rows, the same two chunks each) spread over the banks.
-template <int CPR>
-__device__ __forceinline__ int swz_k(int row) { return row & (CPR - 1); }
-template <int CPR>
-__device__ __forceinline__ int swz_v(int row) { return (row << 1) & (CPR - 2); }
+// When one staged tile serves as both K and V (the latent cache, SHARED), a single
+// swizzle must suit both reads: rotating the row's low four bits left by one maps 16
+// consecutive rows onto all 16 chunk positions (the K reads) and any 8 aligned rows
+// onto 8 distinct chunk pairs (the transposed reads).
+__device__ __forceinline__ int swz_rot4(int row) { return ((row << 1) & 14) | ((row >> 3) & 1); }
+template <int CPR, bool SHARED>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (SHARED) return swz_rot4(row);
+  else return row & (CPR - 1);
+}
+template <int CPR, bool SHARED>
+__device__ __forceinline__ int swz_v(int row) {
+  if constexpr (SHARED) return swz_rot4(row);
+  else return (row << 1) & (CPR - 2);
+}
 
 // One 16-byte direct global->LDS load per lane (nontemporal): lane i of the wave
 // writes LDS bytes [lds_wave_base + 16 i, +16). Device-only: the host pass of this
@@ -248,16 +259,23 @@ struct MfmaCfg {
   static constexpr int CBW = CB / NCW;        // output blocks per wave
   static constexpr int CPR = D / 8;           // 16-byte chunks per row
   static constexpr int ROW_BYTES = D * 2;
+  // D = 512 is the GQLA latent: one staged tile is both K and V
+  static constexpr bool SHARED = D == 512;
   static constexpr int TENSOR_BYTES = T * ROW_BYTES;
-  static constexpr int STAGE_BYTES = 2 * TENSOR_BYTES;
+  static constexpr int STAGE_BYTES = (SHARED ? 1 : 2) * TENSOR_BYTES;
   static constexpr int LOADS = T * CPR / kThreads;  // 16-B loads per thread per tensor
   static constexpr int RPL = kThreads / CPR;        // tile rows covered by one such load
-  static constexpr int LD = 2 * LOADS;              // per thread per stage (K and V)
+  static constexpr int LD = (SHARED ? 1 : 2) * LOADS;  // per thread per stage (K and V)
+  // rows after which the staging swizzles repeat
+  static constexpr int SWZ_ROWS = SHARED ? 16 : CPR;
+  // distinct lane offsets of the staging loads (a load covers RPL rows)
+  static constexpr int KP = RPL % SWZ_ROWS == 0 ? 1 : SWZ_ROWS / RPL;
   static constexpr int LDS_BYTES = NS * STAGE_BYTES;
   static_assert(NRW * NCW == 4, "four waves per workgroup");
   static_assert(KB == 2, "one 32-deep PV product per tile");
   static_assert(LOADS >= 1 && (T * CPR) % kThreads == 0, "stage load split");
   static_assert(CB % NCW == 0, "column split");
+  static_assert(RPL % SWZ_ROWS == 0 || SWZ_ROWS % RPL == 0, "swizzle period and rows per load");
 };
 
 // Position in the flattened tile sequence: segment (b, g, rb) -- row block rb of KV
@@ -392,13 +410,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 
   // Lane-constant part of a staging load: load n of this lane covers tile row
   // n * RPL + rl, 16-byte chunk pch, and fetches global chunk pch ^ swizzle(row). The
-  // swizzles depend on the row modulo CPR, and RPL is a multiple of CPR, so the
-  // offsets within a row block are the same for every n.
+  // swizzles repeat every SWZ_ROWS rows, so load n uses offset n % KP of this lane
+  // (one offset when a load spans whole periods).
   const int rl = tid / CPR;
   const int pch = tid % CPR;
-  const uint32_t koff = (uint32_t)(rl * ROW_BYTES + ((pch ^ swz_k<CPR>(rl)) << 4));
-  const uint32_t voff = (uint32_t)(rl * ROW_BYTES + ((pch ^ swz_v<CPR>(rl)) << 4));
-  static_assert(C::RPL % CPR == 0, "swizzle period divides the rows per load");
+  uint32_t koff[C::KP], voff[C::KP];
+#pragma unroll
+  for (int kp = 0; kp < C::KP; ++kp) {
+    const int row = kp * C::RPL + rl;
+    koff[kp] = (uint32_t)(rl * ROW_BYTES + ((pch ^ swz_k<CPR, C::SHARED>(row)) << 4));
+    voff[kp] = (uint32_t)(rl * ROW_BYTES + ((pch ^ swz_v<CPR, C::SHARED>(row)) << 4));
+  }
 
   auto issue_tile = [&](const Cursor& c, int f) {
     unsigned char* st = smem + (f % NS) * C::STAGE_BYTES;
@@ -421,8 +443,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
           rb = (((size_t)c.b * p.G + c.g) * (size_t)p.capacity + j0) * ROW_BYTES;
         }
         const int lds_off = n * kThreads * 16 + wave * 1024;  // this wave's 64 x 16 B slots
-        load16_to_lds(kg + rb + koff, st + lds_off);
-        load16_to_lds(vg + rb + voff, st + C::TENSOR_BYTES + lds_off);
+        load16_to_lds(kg + rb + koff[n % C::KP], st + lds_off);
+        if constexpr (!C::SHARED) load16_to_lds(vg + rb + voff[n % C::KP], st + C::TENSOR_BYTES + lds_off);
       }
       return;
     }
@@ -445,8 +467,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         }
       }
       const int lds_off = n * kThreads * 16 + wave * 1024;  // this wave's 64 x 16 B slots
-      load16_to_lds(ksrc + ((pch ^ swz_k<CPR>(row)) << 4), st + lds_off);
-      load16_to_lds(vsrc + ((pch ^ swz_v<CPR>(row)) << 4), st + C::TENSOR_BYTES + lds_off);
+      load16_to_lds(ksrc + ((pch ^ swz_k<CPR, C::SHARED>(row)) << 4), st + lds_off);
+      if constexpr (!C::SHARED)
+        load16_to_lds(vsrc + ((pch ^ swz_v<CPR, C::SHARED>(row)) << 4), st + C::TENSOR_BYTES + lds_off);
     }
   };
 
@@ -454,7 +477,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   // back the chunks its own loads placed) into the cache. Called right after the
   // tile's wait, while nothing else is in flight.
   auto copy_new_rows = [&](const Cursor& c, int f) {
-    // every row block of a group stages the same tile; the first one writes it
+    // every row block of a group stages the same tile; the first one writes it (the
+    // latent path has no append: the host never passes new rows with it)
+    if constexpr (C::SHARED) return;
     if (!tile_has_new(c) || c.rb != 0) return;
     const unsigned char* st = smem + (f % NS) * C::STAGE_BYTES;
     const int t0 = c.t * T;
@@ -473,8 +498,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         const u32x4 kv = *reinterpret_cast<const u32x4*>(st + slot);
         const u32x4 vv = *reinterpret_cast<const u32x4*>(st + C::TENSOR_BYTES + slot);
         const size_t rb = cache_row(c, pg, row, j);
-        *reinterpret_cast<u32x4*>(kc + rb + ((pch ^ swz_k<CPR>(row)) << 4)) = kv;
-        *reinterpret_cast<u32x4*>(vc + rb + ((pch ^ swz_v<CPR>(row)) << 4)) = vv;
+        *reinterpret_cast<u32x4*>(kc + rb + ((pch ^ swz_k<CPR, C::SHARED>(row)) << 4)) = kv;
+        *reinterpret_cast<u32x4*>(vc + rb + ((pch ^ swz_v<CPR, C::SHARED>(row)) << 4)) = vv;
       }
     }
   };
@@ -605,7 +630,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       for (int cc = 0; cc < CC; ++cc) {
         const int ch = cc * 4 + g4;
         const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(ks + row * ROW_BYTES + ((ch ^ swz_k<CPR>(row)) << 4));
+            *reinterpret_cast<const bf16x8*>(ks + row * ROW_BYTES + ((ch ^ swz_k<CPR, C::SHARED>(row)) << 4));
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
           s[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][cc], s[rt][kb], 0, 0, 0);
@@ -673,7 +698,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       const int c0 = (cw * CBW + cb) * 16;
       const int r = g4 * 4 + (l16 >> 2);
       const int c = c0 + ((l16 & 3) << 2);
-      return lds_addr(vs + r * ROW_BYTES + ((((c >> 3) ^ swz_v<CPR>(r)) << 4) | ((c & 7) << 1)));
+      return lds_addr(vs + r * ROW_BYTES + ((((c >> 3) ^ swz_v<CPR, C::SHARED>(r)) << 4) | ((c & 7) << 1)));
     };
     bf16x8 pb[RTW];
 #pragma unroll
@@ -728,7 +753,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         for (int cb = 0; cb < CBW; ++cb) {
           const int col = (cw * CBW + cb) * 16 + g4 * 4;
           const f32x4 val = o[rt][cb] * inv;
-          if (complete) {
+          if (complete && p.out_f32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow * D + col) = val;
+          } else if (complete) {
             bf16x4 ov;
 #pragma unroll
             for (int i = 0; i < 4; ++i) ov[i] = (__bf16)val[i];
@@ -791,7 +818,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     }
     const unsigned char* ks = smem + (f % NS) * C::STAGE_BYTES;
     const int tile0 = cons.t * T;
-    consume(ks, ks + C::TENSOR_BYTES, tile0, tile0 + T - 1 > lim_min);
+    consume(ks, C::SHARED ? ks : ks + C::TENSOR_BYTES, tile0, tile0 + T - 1 > lim_min);
     const bool seg_end = cons.t == cons.n - 1;
     if (seg_end || f == count - 1) {
       const bool complete = seg_from_start && seg_end;
@@ -832,12 +859,22 @@ int variant_occupancy(bool paged) {
   X(128, 4, 1, 2)            \
   X(256, 4, 1, 4)
 
+// The 512-wide latent (K = V, staged once): up to 32 rows per workgroup, the query
+// fragments alone taking 64 registers per row tile.
+#define GQA_MFMA_LATENT_VARIANTS(X) \
+  X(16, 1, 4, 1)                    \
+  X(32, 2, 2, 1)
+
 template <int D>
 hipError_t launch_for_rows(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream, hipEvent_t start,
                            hipEvent_t stop) {
 #define X(ROWS, NRW, NCW, RTW) \
   if (p.row_block <= ROWS) return launch_variant<D, NRW, NCW, RTW>(p, paged, grid, stream, start, stop);
-  GQA_MFMA_VARIANTS(X)
+  if constexpr (D == 512) {
+    GQA_MFMA_LATENT_VARIANTS(X)
+  } else {
+    GQA_MFMA_VARIANTS(X)
+  }
 #undef X
   return hipErrorInvalidValue;
 }
@@ -848,7 +885,11 @@ MfmaVariant variant_for(int R, bool paged, bool query_device) {
   if (R <= ROWS)                                                                                     \
     return MfmaVariant{ROWS, kTile, MfmaCfg<D, NRW, NCW, RTW>::LDS_BYTES,                            \
                        query_device ? variant_occupancy<D, NRW, NCW, RTW>(paged) : 0};
-  GQA_MFMA_VARIANTS(X)
+  if constexpr (D == 512) {
+    GQA_MFMA_LATENT_VARIANTS(X)
+  } else {
+    GQA_MFMA_VARIANTS(X)
+  }
 #undef X
   return MfmaVariant{0, kTile, 0, 0};
 }
@@ -856,12 +897,16 @@ MfmaVariant variant_for(int R, bool paged, bool query_device) {
 }  // namespace
 
 MfmaVariant mfma_variant_for_rows(int R, int d_h, bool paged, bool query_device) {
+  if (d_h == 512) return variant_for<512>(R, paged, query_device);
   return d_h == 64 ? variant_for<64>(R, paged, query_device) : variant_for<128>(R, paged, query_device);
 }
+
+int mfma_max_rows(int d_h) { return d_h == 512 ? 32 : 256; }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int dtype, int d_h, bool paged, dim3 grid,
                               hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   (void)dtype;  // bf16 only (checked by the planner)
+  if (d_h == 512) return launch_for_rows<512>(p, paged, grid, stream, start, stop);
   if (d_h == 64) return launch_for_rows<64>(p, paged, grid, stream, start, stop);
   return launch_for_rows<128>(p, paged, grid, stream, start, stop);
 }

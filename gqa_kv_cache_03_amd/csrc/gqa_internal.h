@@ -39,6 +39,7 @@ struct DecodeParams {
   int n_row_blocks;
   int nwg;                 // persistent workgroups (MFMA policy)
   float qk_scale_log2;     // scale * log2(e): logits in base-2 units
+  int out_f32;             // write `out` as float32 instead of the input dtype (latent path)
 };
 
 // Row r of the packed group tile is query token t = r / hpg of head g*hpg + r % hpg.
@@ -58,6 +59,19 @@ hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t s
 // Writes k_new / v_new into the cache rows of the new tokens (vector-ALU path).
 hipError_t launch_append(const DecodeParams& p, int elem_bytes, int d_h, bool paged, hipStream_t stream);
 
+// GQLA latent path: the per-group projections around the latent attention.
+struct LatentProjParams {
+  const void* q;        // [rows, d_h] bf16, rows = B * q_len * H (row = (b q_len + t) H + h)
+  const void* w_uk;     // [G, d_h, d_c] bf16
+  const void* w_uv;     // [G, d_h, d_c] bf16
+  void* q_lat;          // [rows, d_c] bf16: q folded through its group's W_UK
+  const float* u;       // [rows, d_c] float32: attention-weighted latent
+  void* out;            // [rows, d_h] bf16
+  int B, H, G, q_len, d_h, d_c;
+};
+hipError_t launch_latent_absorb_q(const LatentProjParams& p, hipStream_t stream);
+hipError_t launch_latent_up_proj(const LatentProjParams& p, hipStream_t stream);
+
 // Geometry of the MFMA kernel variants, chosen by packed row count R.
 struct MfmaVariant {
   int max_rows;      // R this variant serves (multiple of 16)
@@ -66,6 +80,8 @@ struct MfmaVariant {
   int wgs_per_cu;    // resident workgroups per CU (0 when not queried / no device)
 };
 MfmaVariant mfma_variant_for_rows(int R, int d_h, bool paged, bool query_device);
+// Most packed rows one MFMA workgroup holds at this head width (d_h 512: the latent).
+int mfma_max_rows(int d_h);
 int valu_tile_tokens(int dtype, int d_h);
 int valu_lds_bytes(int dtype, int d_h, int row_block);
 

@@ -255,7 +255,10 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
     lt += wt * sm_l[k];
   }
   const float inv = (lt > 0.f && on) ? 1.f / lt : 0.f;
-  put4<__bf16>(static_cast<__bf16*>(p.out) + orow * D + c, tot * inv);
+  if (p.out_f32)
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow * D + c) = tot * inv;
+  else
+    put4<__bf16>(static_cast<__bf16*>(p.out) + orow * D + c, tot * inv);
 }
 
 template <int D>
@@ -269,6 +272,7 @@ hipError_t go_persistent(const DecodeParams& p, hipStream_t stream, hipEvent_t s
 
 hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t stream, hipEvent_t start,
                                    hipEvent_t stop) {
+  if (d_h == 512) return go_persistent<512>(p, stream, start, stop);
   return d_h == 64 ? go_persistent<64>(p, stream, start, stop) : go_persistent<128>(p, stream, start, stop);
 }
 

@@ -208,3 +208,95 @@ def read_stream(buf, sink=None, workgroups: int = 0) -> None:
         st = L.gqa_bench_read_stream_lds(buf.data_ptr(), nbytes, workgroups, stream)
     if st != _lib.GQA_OK:
         raise GqaError(st, "gqa_bench_read_stream")
+
+
+def _latent_geometry(q, latent_cache, w_uk, block_table):
+    B, q_len, H, d_h = q.shape
+    if w_uk.dim() != 3 or w_uk.shape[1] != d_h:
+        raise ValueError("w_uk must be [G, d_h, d_c]")
+    G, d_c = w_uk.shape[0], w_uk.shape[2]
+    if block_table is None:
+        if latent_cache.dim() != 3 or latent_cache.shape[0] != B or latent_cache.shape[2] != d_c:
+            raise ValueError("contiguous latent cache must be [B, capacity, d_c]")
+        return B, q_len, H, d_h, G, d_c, dict(capacity=latent_cache.shape[1])
+    if latent_cache.dim() != 3 or latent_cache.shape[2] != d_c:
+        raise ValueError("paged latent pool must be [num_pages, page_size, d_c]")
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [B, max_blocks_per_seq]")
+    return B, q_len, H, d_h, G, d_c, dict(capacity=0, page_size=latent_cache.shape[1],
+                                          max_blocks=block_table.shape[1], num_pages=latent_cache.shape[0])
+
+
+def gqla_plan(q, latent_cache, w_uk, block_table=None, *, causal=True, num_splits=0, policy="auto") -> dict:
+    """What gqla_absorb_decode would launch for these tensors (no device work)."""
+    import torch
+    B, q_len, H, d_h, G, d_c, geo = _latent_geometry(q, latent_cache, w_uk, block_table)
+    o = make_opts(dtype_code=_dtype_code(torch, q.dtype), causal=causal, num_splits=num_splits, policy=policy,
+                  **geo)
+    pl = Plan()
+    st = _lib.lib().gqla_absorb_plan(B, H, G, d_h, d_c, q_len, ctypes.byref(o), ctypes.byref(pl))
+    if st != _lib.GQA_OK:
+        raise GqaError(st, "gqla_absorb_plan")
+    return pl.as_dict()
+
+
+def gqla_absorb_decode(q, latent_cache, w_uk, w_uv, seq_lens, block_table=None, *,
+                       scale: Optional[float] = None, out=None, causal: bool = True, num_splits: int = 0,
+                       policy: str = "auto", workspace=None, profile_events=None):
+    """One decode step of a GQLA layer in its absorbed (MQA) form.
+
+    q [B, q_len, H, d_h] bf16; latent_cache [B, capacity, d_c] (or a paged pool
+    [num_pages, page_size, d_c] with block_table [B, max_blocks]); w_uk, w_uv
+    [G, d_h, d_c]; seq_lens int32 [B]. Returns out [B, q_len, H, d_h]: attention of
+    each head over its group's expanded cache W c_j, computed against the latent.
+    """
+    import torch
+    tensors = [("q", q), ("latent_cache", latent_cache), ("w_uk", w_uk), ("w_uv", w_uv), ("seq_lens", seq_lens)]
+    for name, t in tensors:
+        if t is None:
+            raise ValueError(f"{name} is required")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    for name, t in tensors[1:4]:
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} must have q's dtype")
+    if w_uv.shape != w_uk.shape:
+        raise ValueError("w_uk and w_uv must have the same shape")
+    if seq_lens.dtype != torch.int32:
+        raise TypeError("seq_lens must be int32")
+    if block_table is not None and (block_table.dtype != torch.int32 or not block_table.is_contiguous()
+                                    or not block_table.is_cuda):
+        raise TypeError("block_table must be a contiguous int32 device tensor")
+    B, q_len, H, d_h, G, d_c, geo = _latent_geometry(q, latent_cache, w_uk, block_table)
+    if seq_lens.numel() != B:
+        raise ValueError("seq_lens must have B entries")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_h)
+    o = make_opts(dtype_code=_dtype_code(torch, q.dtype), causal=causal, num_splits=num_splits, policy=policy,
+                  **geo)
+    L = _lib.lib()
+    need = ctypes.c_size_t(0)
+    st = L.gqla_absorb_workspace_size(B, H, G, d_h, d_c, q_len, ctypes.byref(o), ctypes.byref(need))
+    if st != _lib.GQA_OK:
+        raise GqaError(st, "gqla_absorb_workspace_size")
+    if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    o.workspace = workspace.data_ptr()
+    o.workspace_bytes = workspace.numel() * workspace.element_size()
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if profile_events is not None:
+        for i, ev in enumerate(profile_events):
+            o.profile_events[i] = ev
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    bt = None if block_table is None else block_table.data_ptr()
+    st = L.gqla_absorb_decode(q.data_ptr(), latent_cache.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+                              seq_lens.data_ptr(), bt, out.data_ptr(), B, H, G, d_h, d_c, q_len,
+                              ctypes.c_float(scale), stream, ctypes.byref(o))
+    if st != _lib.GQA_OK:
+        raise GqaError(st, "gqla_absorb_decode")
+    return out

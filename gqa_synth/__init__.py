@@ -11,6 +11,8 @@ from .generate import (
     draw_block_table,
     make_inputs,
     DecodeInputs,
+    make_latent_inputs,
+    LatentInputs,
 )
 
 __all__ = [
@@ -23,4 +25,6 @@ __all__ = [
     "draw_block_table",
     "make_inputs",
     "DecodeInputs",
+    "make_latent_inputs",
+    "LatentInputs",
 ]

@@ -15,6 +15,11 @@ Recipe (stated once here, used by every test and the benchmark):
   pages, taken in order from one seeded permutation of all page ids (entropy
   (seed, 4)); the block table is [B, ceil(len_hi / P)] int32 with -1 in unused
   entries; unused page slots and extra pages hold NaN.
+* GQLA layers (d_c > 0): q as above; the latent of sequence b is N(0, 1) fp32 draws
+  [L_b, d_c] seeded from (seed, 6, b), rounded to bf16, in a contiguous [B, cap, d_c]
+  cache or a paged pool [num_pages, page_size, d_c] laid out as above; W_UK and W_UV
+  are N(0, 1) / sqrt(d_c) draws [G, d_h, d_c] seeded from (seed, 7) and (seed, 8)
+  (unit-variance keys and values), rounded to bf16.
 """
 from __future__ import annotations
 
@@ -25,7 +30,7 @@ import numpy as np
 
 from .workloads import Workload
 
-STREAM_Q, STREAM_K, STREAM_V, STREAM_LENS, STREAM_PERM, STREAM_KNORM = range(6)
+STREAM_Q, STREAM_K, STREAM_V, STREAM_LENS, STREAM_PERM, STREAM_KNORM, STREAM_LAT, STREAM_WUK, STREAM_WUV = range(9)
 
 
 def _rng(*entropy: int) -> np.random.Generator:
@@ -184,3 +189,66 @@ def paginate(torch, k_contig, lens, page_size, seed, extra_pages=0, fill=float("
         pos += n
         _scatter_pages(torch, pool, k_contig[b, :, :int(lens[b])], table[b], P, k_contig.device)
     return pool, table, num_pages
+
+
+@dataclass
+class LatentInputs:
+    wl: Workload
+    q: "object"                 # torch.Tensor [B, q_len, H, d_h]
+    latent: "object"            # contiguous [B, cap, d_c] or paged [pages, P, d_c]
+    w_uk: "object"              # [G, d_h, d_c]
+    w_uv: "object"
+    seq_lens: "object"          # torch int32 [B]
+    block_table: "object"       # torch int32 [B, max_blocks] or None
+    lens: np.ndarray
+    table: Optional[np.ndarray]
+    capacity: int
+    num_pages: int
+
+    @property
+    def latent_bytes(self) -> int:
+        """Latent bytes the absorbed step must read: d_c * itemsize * sum_b L_b."""
+        return self.wl.d_c * self.wl.itemsize * int(self.lens.astype(np.int64).sum())
+
+
+def make_latent_inputs(wl: Workload, device="cpu", lens: Optional[np.ndarray] = None,
+                       nan_fill: bool = True) -> LatentInputs:
+    """Materialise a GQLA workload (d_c > 0) on `device`."""
+    import torch
+
+    assert wl.d_c > 0, "not a GQLA workload"
+    dt = _torch_dtype(torch, wl.dtype)
+    lens = draw_lengths(wl) if lens is None else np.asarray(lens, dtype=np.int32)
+    assert lens.shape == (wl.B,)
+    d_c = wl.d_c
+    fill = float("nan") if nan_fill else 0.0
+    q = _normal(torch, (wl.B, wl.q_len, wl.H, wl.d_h), _torch_seed(wl.seed, STREAM_Q), device).to(dt)
+    w_uk = (_normal(torch, (wl.G, wl.d_h, d_c), _torch_seed(wl.seed, STREAM_WUK), device) / np.sqrt(d_c)).to(dt)
+    w_uv = (_normal(torch, (wl.G, wl.d_h, d_c), _torch_seed(wl.seed, STREAM_WUV), device) / np.sqrt(d_c)).to(dt)
+    table = None
+    if wl.layout == "paged":
+        table, num_pages = draw_block_table(wl, lens)
+        P = wl.page_size
+        latent = torch.full((num_pages, P, d_c), fill, dtype=dt, device=device)
+        capacity = table.shape[1] * P
+    else:
+        num_pages = 0
+        capacity = max(wl.len_hi, int(lens.max()))
+        latent = torch.full((wl.B, capacity, d_c), fill, dtype=dt, device=device)
+    for b in range(wl.B):
+        L = int(lens[b])
+        cb = _normal(torch, (L, d_c), _torch_seed(wl.seed, STREAM_LAT, b), device).to(dt)
+        if table is None:
+            latent[b, :L] = cb
+        else:
+            P = wl.page_size
+            n_full = L // P
+            if n_full:
+                pages = torch.as_tensor(table[b, :n_full].astype(np.int64), device=device)
+                latent[pages] = cb[:n_full * P].reshape(n_full, P, d_c)
+            if L - n_full * P:
+                latent[int(table[b, n_full]), :L - n_full * P] = cb[n_full * P:]
+        del cb
+    seq_lens = torch.as_tensor(lens, dtype=torch.int32, device=device)
+    bt = None if table is None else torch.as_tensor(table, dtype=torch.int32, device=device)
+    return LatentInputs(wl, q, latent, w_uk, w_uv, seq_lens, bt, lens, table, capacity, num_pages)

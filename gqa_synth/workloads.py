@@ -31,6 +31,8 @@ class Workload:
     causal: bool = True
     seed: int = 0
     extra_pages: int = 0         # unused pool pages (NaN-filled) for paged layouts
+    d_c: int = 0                 # >0: a GQLA layer -- one latent of d_c per token, G groups
+                                 #     of up-projections [G, d_h, d_c] (absorbed execution)
     description: str = field(default="", compare=False)
 
     @property
@@ -39,7 +41,10 @@ class Workload:
 
     @property
     def R(self) -> int:
-        """Query rows that share one KV head in one step: (H/G) * q_len."""
+        """Query rows that share one KV head in one step: (H/G) * q_len; for a GQLA
+        layer in its absorbed form every head reads the one latent: H * q_len."""
+        if self.d_c:
+            return self.H * self.q_len
         return self.heads_per_group * self.q_len
 
     @property
@@ -112,6 +117,24 @@ for _w in [
         B=8, H=32, G=1, d_h=128, q_len=16, dtype="bfloat16",
         len_lo=32768 + 16, len_hi=32768 + 16, layout="paged", page_size=32, seed=1006,
         description="16 new tokens (causal among them), MQA, 32-token pages",
+    ),
+    # GQLA (thelatestinai page for 2604.07766): the abstract measures the absorbed and
+    # the expanded execution on eight GPUs with tensor parallelism over 8K-64K inputs;
+    # one GPU's share at TP 8 of a layer with 128 query heads in groups of eight holds
+    # 16 heads in 2 groups and the whole latent (absorption replicates it). The
+    # second workload is the same share run as plain GQA over the expanded cache, which
+    # holds 2 x 2 x 128 = 512 numbers per token, as many as the latent.
+    Workload(
+        name="gqla_absorb_tp8_bf16_B16_H16_G2_d128_c512_n8k_64k",
+        B=16, H=16, G=2, d_h=128, q_len=1, dtype="bfloat16",
+        len_lo=8192, len_hi=65536, layout="paged", page_size=16, seed=1008, d_c=512,
+        description="GQLA absorbed: 16 heads over one 512-wide latent, 16-token pages",
+    ),
+    Workload(
+        name="gqla_expanded_tp8_bf16_B16_H16_G2_d128_n8k_64k",
+        B=16, H=16, G=2, d_h=128, q_len=1, dtype="bfloat16",
+        len_lo=8192, len_hi=65536, layout="paged", page_size=16, seed=1008,
+        description="the same GQLA share run as GQA over the expanded per-group cache",
     ),
     Workload(
         name="spec16_paged32_bf16_B8_H32_G4_d128_n32k",

@@ -20,10 +20,10 @@ P = 4096  # a fake, aligned, non-null address: validation never dereferences it
 
 def declared_symbols():
     names = set()
-    for h in ("gqa_decode.h", "gqa_bench.h"):
+    for h in ("gqa_decode.h", "gqa_bench.h", "gqla_absorb.h"):
         txt = open(os.path.join(ROOT, "include", h)).read()
         txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-        for m in re.finditer(r"\b(?:int|void|size_t|const char\*)\s+(gqa_\w+)\s*\(", txt):
+        for m in re.finditer(r"\b(?:int|void|size_t|const char\*)\s+(gql?a_\w+)\s*\(", txt):
             names.add(m.group(1))
     return names
 
@@ -262,3 +262,73 @@ def test_grouping_variant_checks():
     assert st == OK and pl.policy == _lib.GQA_POLICY_MFMA
     assert plan(H=8, G=2, o=opts(reserved0=1))[0] == INV
     assert plan(H=40, G=6)[0] == INV                                      # no map: H % G must be 0
+
+
+# --------------------------------------------- GQLA, absorbed execution
+
+def lcall(B=2, H=16, G=2, d=128, d_c=512, q_len=1, scale=0.1, o=None, q=P, lat=P, wk=P, wv=P, sl=P, bt=None,
+          out=P):
+    o = opts() if o is None else o
+    return _lib.lib().gqla_absorb_decode(q, lat, wk, wv, sl, bt, out, B, H, G, d, d_c, q_len, ctypes.c_float(scale),
+                                         None, ctypes.byref(o) if o is not False else None)
+
+
+def lplan(B=2, H=16, G=2, d=128, d_c=512, q_len=1, o=None):
+    o = opts() if o is None else o
+    pl = Plan()
+    st = _lib.lib().gqla_absorb_plan(B, H, G, d, d_c, q_len, ctypes.byref(o), ctypes.byref(pl))
+    return st, pl
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INV), (dict(lat=None), INV), (dict(wk=None), INV), (dict(wv=None), INV),
+    (dict(sl=None), INV), (dict(out=None), INV), (dict(wk=P + 8), INV), (dict(lat=P + 2), INV),
+    (dict(B=0), INV), (dict(H=0), INV), (dict(G=0), INV), (dict(d=0), INV), (dict(d_c=0), INV),
+    (dict(q_len=0), INV), (dict(H=16, G=3), INV), (dict(H=2, G=4), INV),
+    (dict(scale=float("nan")), INV),
+    (dict(d=96), UNS), (dict(d_c=256), UNS), (dict(d_c=576), UNS),
+    (dict(H=128, q_len=9), UNS),                     # H q_len = 1152 > 1024 rows
+    (dict(o=False), INV),
+])
+def test_latent_invalid_arguments_are_rejected(kw, status):
+    assert lcall(**kw) == status
+
+
+def test_latent_opts_checks():
+    assert lcall(o=opts(dtype=_lib.GQA_DTYPE_F32)) == UNS
+    assert lcall(o=opts(policy=_lib.GQA_POLICY_VALU)) == UNS
+    assert lcall(o=opts(head_active=P)) == UNS
+    assert lcall(o=opts(head_group=P)) == UNS
+    assert lcall(o=opts(page_size=16)) == INV          # page size without a block table
+    assert lcall() == WS                               # the workspace is always needed
+
+
+@pytest.mark.parametrize("H,G,q_len,rows,blocks", [(16, 2, 1, 16, 1), (16, 16, 2, 32, 1), (128, 16, 1, 128, 4),
+                                                   (8, 1, 3, 24, 1), (40, 5, 1, 40, 2)])
+def test_latent_plan(H, G, q_len, rows, blocks):
+    """Every query head reads the one latent: H q_len rows, in blocks of at most 32
+    (the 512-wide query fragments fill the registers); the workspace holds the
+    absorbed queries (bf16), the weighted latents (fp32) and the split partials."""
+    B = 3
+    st, pl = lplan(B=B, H=H, G=G, q_len=q_len, o=opts(num_splits=100))
+    assert st == OK
+    assert pl.policy == _lib.GQA_POLICY_MFMA and pl.schedule == 1
+    assert pl.rows == rows and pl.row_blocks == blocks and pl.workgroups == 100
+    rb = -(-rows // blocks)
+    rb = rows if blocks == 1 else -(-rb // 16) * 16
+    up = lambda x: -(-x // 256) * 256  # noqa: E731
+    n = B * q_len * H
+    attn = up(100 * 2 * rb * 512 * 4) + up(100 * 2 * rb * 4) + up((B + 1) * 4)
+    assert pl.workspace_bytes == up(n * 512 * 2) + up(n * 512 * 4) + attn
+    assert pl.lds_bytes == 2 * 32 * 512 * 2          # two stages of 32 latent rows, staged once
+    size = ctypes.c_size_t(0)
+    o = opts(num_splits=100)
+    assert _lib.lib().gqla_absorb_workspace_size(B, H, G, 128, 512, q_len, ctypes.byref(o), ctypes.byref(size)) == OK
+    assert size.value == pl.workspace_bytes
+
+
+def test_latent_paged_geometry_checks():
+    good = dict(page_size=16, max_blocks_per_seq=8, num_pages=40, num_splits=1)
+    assert lcall(bt=P, o=opts(**good)) == WS              # valid; only the workspace is missing
+    for bad in (dict(page_size=8), dict(max_blocks_per_seq=0), dict(num_pages=0)):
+        assert lcall(bt=P, o=opts(**{**good, **bad})) == INV, bad
