@@ -3,15 +3,16 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--append]
 
-A step is one gqa_decode call (gqa_decode_append with --append) over the whole batch
-of the workload, inputs resident in HBM. Several copies of the KV cache are rotated so that every step reads cold data
-(the 256 MiB Infinity Cache cannot serve a step from the previous one). Prints one
-JSON line:
+A step is one gqa_decode call (gqa_decode_append with --append; gqla_absorb_decode for
+a GQLA workload) over the whole batch of the workload, inputs resident in HBM. Several
+copies of the cache are rotated so that every step reads cold data (the 256 MiB
+Infinity Cache cannot serve a step from the previous one). Prints one JSON line:
 
-  value      KV GB/s = 2 * G * d_h * itemsize * sum(seq_lens) / (time per step)
+  value      KV GB/s = 2 * G * d_h * itemsize * sum(seq_lens) / (time per step); for a
+             GQLA workload the latent's d_c * itemsize * sum(seq_lens)
   roofline   the decode kernel's algorithmic bytes over its own duration (HIP events
-             recorded by the library on the launch stream) against MI355X's 8 TB/s
-             HBM peak
+             that its launch stamps) against MI355X's 8 TB/s HBM peak, or its matrix
+             work against the 2.5 PFLOP/s bf16 peak when that bounds it
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -165,6 +166,49 @@ def cpu_baseline(inp, budget_s: float):
     }
 
 
+def cpu_baseline_latent(inp, budget_s: float):
+    """The GQLA oracle, as it is, on whole sequences in order (starting over when a
+    pass ends sooner) until the budget is spent; KV GB/s counts the latent bytes."""
+    import numpy as np
+    import oracle
+    wl = inp.wl
+    wk = inp.w_uk.float().cpu().numpy()
+    wv = inp.w_uv.float().cpu().numpy()
+    done_bytes, elapsed, units = 0, 0.0, 0
+    while units == 0 or elapsed < budget_s:
+        for b in range(wl.B):
+            L = int(inp.lens[b])
+            q = inp.q[b:b + 1].float().cpu().numpy()
+            if inp.block_table is None:
+                lat = inp.latent[b:b + 1, :L].float().cpu().numpy()
+            else:
+                import torch
+                n = -(-L // wl.page_size)
+                pages = torch.as_tensor(inp.table[b, :n].astype(np.int64), device=inp.latent.device)
+                lat = inp.latent[pages].reshape(1, n * wl.page_size, wl.d_c)[:, :L].float().cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.gqla_decode(q, lat, wk, wv, inp.lens[b:b + 1], wl.scale, causal=wl.causal)
+            elapsed += time.perf_counter() - t0
+            done_bytes += wl.d_c * wl.itemsize * L
+            units += 1
+            if elapsed >= budget_s:
+                break
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        avail = os.cpu_count()
+    return {
+        "value": round(done_bytes / elapsed / 1e9, 4),
+        "unit": "GB/s",
+        "cores": avail,
+        "kind": "oracle",
+        "sample": (f"{units} sequences in order ({units / wl.B:.2f} passes over the workload's {wl.B}), "
+                   f"{elapsed:.1f} s of fp64 numpy oracle time (expanding the latent, then attention); "
+                   f"{done_bytes / 1e6:.1f} MB of latent; host fp32 copies of the inputs; {avail} cores visible"),
+        "tokens_per_s_equiv": round(units / wl.B * wl.B * wl.q_len / elapsed, 3),
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -177,22 +221,30 @@ def main():
     import numpy as np
     import torch
 
-    from gqa_kv_cache_03_amd import gqa_decode, gqa_decode_append, plan, read_stream
-    from gqa_synth import BENCH_DEFAULT, make_inputs, workload
+    from gqa_kv_cache_03_amd import gqa_decode, gqa_decode_append, gqla_absorb_decode, gqla_plan, plan, read_stream
+    from gqa_synth import BENCH_DEFAULT, make_inputs, make_latent_inputs, workload
 
     name = args.workload or BENCH_DEFAULT
     wl = workload(name)
+    latent = bool(wl.d_c)   # a GQLA layer, run in its absorbed form
+    if latent and (args.append or args.head_map or args.active_frac > 0 or args.policy == "valu"):
+        sys.exit("the GQLA absorbed path takes no --append, --head-map, --active-frac or valu policy")
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     print(f"[bench] generating {name}", file=sys.stderr, flush=True)
-    inp = make_inputs(wl, device=dev)
-    kv_bytes = inp.kv_bytes
-    alloc_bytes = inp.k_cache.numel() * inp.k_cache.element_size() * 2
+    if latent:
+        inp = make_latent_inputs(wl, device=dev)
+        kv_bytes = inp.latent_bytes
+        caches = [inp.latent]
+    else:
+        inp = make_inputs(wl, device=dev)
+        kv_bytes = inp.kv_bytes
+        caches = [inp.k_cache, inp.v_cache]
+    alloc_bytes = sum(c.numel() * c.element_size() for c in caches)
     copies = args.copies or max(1, min(8, math.ceil((1 << 30) / alloc_bytes)))
-    ks, vs = [inp.k_cache], [inp.v_cache]
-    for _ in range(copies - 1):
-        ks.append(inp.k_cache.clone())
-        vs.append(inp.v_cache.clone())
+    # ks[i] / vs[i]: the i-th rotated copy of the cache (the latent: ks only)
+    ks = [caches[0]] + [caches[0].clone() for _ in range(copies - 1)]
+    vs = [] if latent else [caches[1]] + [caches[1].clone() for _ in range(copies - 1)]
     out = torch.empty_like(inp.q)
     variant = {}
     if args.head_map:
@@ -211,10 +263,15 @@ def main():
         rng = np.random.default_rng(wl.seed + 8)
         act = (rng.random((wl.B, wl.q_len, wl.H)) < args.active_frac).astype(np.uint8)
         variant["head_active"] = torch.as_tensor(act, device=dev)
-    kw = dict(scale=wl.scale, causal=wl.causal, num_splits=args.num_splits, chunk_tokens=args.chunk,
-              policy=args.policy, **variant)
-    pl = plan(inp.q, inp.k_cache, inp.block_table, causal=wl.causal, num_splits=args.num_splits,
-              chunk_tokens=args.chunk, policy=args.policy, **variant)
+    if latent:
+        kw = dict(scale=wl.scale, causal=wl.causal, num_splits=args.num_splits, policy=args.policy)
+        pl = gqla_plan(inp.q, inp.latent, inp.w_uk, inp.block_table, causal=wl.causal,
+                       num_splits=args.num_splits, policy=args.policy)
+    else:
+        kw = dict(scale=wl.scale, causal=wl.causal, num_splits=args.num_splits, chunk_tokens=args.chunk,
+                  policy=args.policy, **variant)
+        pl = plan(inp.q, inp.k_cache, inp.block_table, causal=wl.causal, num_splits=args.num_splits,
+                  chunk_tokens=args.chunk, policy=args.policy, **variant)
     ws = torch.empty(max(pl["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
 
     new_bytes = 0
@@ -233,7 +290,10 @@ def main():
         new_bytes = 2 * k_new.numel() * k_new.element_size()
 
     def step(i, events=None):
-        if args.append:
+        if latent:
+            gqla_absorb_decode(inp.q, ks[i % copies], inp.w_uk, inp.w_uv, inp.seq_lens, inp.block_table,
+                               out=out, workspace=ws, profile_events=events, **kw)
+        elif args.append:
             gqa_decode_append(inp.q, k_new, v_new, ks[i % copies], vs[i % copies], inp.seq_lens,
                               inp.block_table, out=out, workspace=ws, profile_events=events, **kw)
         else:
@@ -273,7 +333,8 @@ def main():
     dec_ms = statistics.mean(dec)
     mrg_ms = statistics.mean(mrg)
 
-    q_bytes = inp.q.numel() * inp.q.element_size()
+    # the queries the decode kernel reads (the latent path: the absorbed, d_c-wide ones)
+    q_bytes = inp.q.numel() * inp.q.element_size() * (wl.d_c // wl.d_h if latent else 1)
     tbl_bytes = 0 if inp.table is None else 4 * int(sum(-(-int(L) // wl.page_size) for L in inp.lens))
     # with the append, the new rows are read from k_new/v_new instead of the cache (same
     # count) and written to the cache once
@@ -311,7 +372,8 @@ def main():
     # useful matrix work of the decode kernel: QK^T and PV, 2 * 2 * d_h flop per
     # (query row, visible key) -- counted over all L keys (the causal triangle among
     # the q_len new tokens is a negligible correction)
-    flops = 4 * wl.H * wl.q_len * wl.d_h * int(sum(int(L) for L in inp.lens))
+    width = wl.d_c if latent else wl.d_h   # the attention's head width (the latent's for GQLA)
+    flops = 4 * wl.H * wl.q_len * width * int(sum(int(L) for L in inp.lens))
     tflops = flops / (dec_ms * 1e-3) / 1e12
     intensity = flops / dec_alg_bytes
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
@@ -328,11 +390,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bfloat16" else "f32",
-        "data": "synthetic (seeded N(0,1) q/K/V, seeded lengths and block tables)",
+        "data": ("synthetic (seeded N(0,1) q and latent, N(0,1/d_c) up-projections, seeded lengths and "
+                 "block tables)" if latent else "synthetic (seeded N(0,1) q/K/V, seeded lengths and block tables)"),
         "config": {
             "workload": name + (" +append" if args.append else "") + (" +head_map" if args.head_map else "")
             + (f" +active{args.active_frac:g}" if args.active_frac > 0 else ""),
-            "B": wl.B, "H": wl.H, "G": wl.G, "d_h": wl.d_h, "q_len": wl.q_len,
+            "B": wl.B, "H": wl.H, "G": wl.G, "d_h": wl.d_h, "q_len": wl.q_len, "d_c": wl.d_c or None,
             "layout": wl.layout, "page_size": wl.page_size or None,
             "lengths": [wl.len_lo, wl.len_hi], "sum_seq_lens": int(inp.lens.sum()),
             "kv_bytes": int(kv_bytes), "kv_copies_rotated": copies, "plan": pl,
@@ -362,7 +425,7 @@ def main():
     del ks, vs
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline_latent(inp, args.cpu_budget) if latent else cpu_baseline(inp, args.cpu_budget)
     print(json.dumps(res), flush=True)
 
 

@@ -270,12 +270,20 @@ struct MfmaCfg {
   static constexpr int SWZ_ROWS = SHARED ? 16 : CPR;
   // distinct lane offsets of the staging loads (a load covers RPL rows)
   static constexpr int KP = RPL % SWZ_ROWS == 0 ? 1 : SWZ_ROWS / RPL;
-  static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+  // The latent's 512-wide scores: the waves that share a row slice split the QK^T
+  // reduction over d (each reads a quarter or half of the K tile instead of all of it)
+  // and add their partial scores through LDS, instead of each repeating all of it.
+  static constexpr bool SPLIT_S = SHARED && NCW > 1;
+  static constexpr int CCW = SPLIT_S ? CC / NCW : CC;      // QK^T k-steps per wave
+  static constexpr int XCH_BYTES = SPLIT_S ? 4 * 64 * RTW * KB * 16 : 0;  // partial scores
+  static constexpr int RING_BYTES = NS * STAGE_BYTES;
+  static constexpr int LDS_BYTES = RING_BYTES + XCH_BYTES;
   static_assert(NRW * NCW == 4, "four waves per workgroup");
   static_assert(KB == 2, "one 32-deep PV product per tile");
   static_assert(LOADS >= 1 && (T * CPR) % kThreads == 0, "stage load split");
   static_assert(CB % NCW == 0, "column split");
   static_assert(RPL % SWZ_ROWS == 0 || SWZ_ROWS % RPL == 0, "swizzle period and rows per load");
+  static_assert(!SPLIT_S || CC % NCW == 0, "QK^T split");
 };
 
 // Position in the flattened tile sequence: segment (b, g, rb) -- row block rb of KV
@@ -505,7 +513,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   };
 
   // ---- 3. per-segment state ----
-  bf16x8 qf[RTW][CC];
+  // query fragments: k-steps cc0 .. cc0 + CCW - 1 of QK^T (all of them unless split)
+  constexpr int CCW = C::CCW;
+  const int cc0 = C::SPLIT_S ? cw * CCW : 0;
+  bf16x8 qf[RTW][CCW];
   float m_run[RTW], l_run[RTW];
   f32x4 o[RTW][CBW];
   int lim[RTW];
@@ -603,13 +614,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         const int h = row_h[rt];
         const __bf16* qrow = static_cast<const __bf16*>(p.q) + ((size_t)(c.b * p.q_len + t) * p.H + h) * D;
 #pragma unroll
-        for (int cc = 0; cc < CC; ++cc) {
-          const u32x4 bits = *reinterpret_cast<const u32x4*>(qrow + cc * 32 + g4 * 8) ^ q_sign;
+        for (int cc = 0; cc < CCW; ++cc) {
+          const u32x4 bits = *reinterpret_cast<const u32x4*>(qrow + (cc0 + cc) * 32 + g4 * 8) ^ q_sign;
           qf[rt][cc] = __builtin_bit_cast(bf16x8, bits);
         }
       } else {
 #pragma unroll
-        for (int cc = 0; cc < CC; ++cc) qf[rt][cc] = bf16x8{};
+        for (int cc = 0; cc < CCW; ++cc) qf[rt][cc] = bf16x8{};
       }
     }
   };
@@ -627,13 +638,37 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     for (int kb = 0; kb < KB; ++kb) {
       const int row = kb * 16 + l16;
 #pragma unroll
-      for (int cc = 0; cc < CC; ++cc) {
-        const int ch = cc * 4 + g4;
+      for (int cc = 0; cc < CCW; ++cc) {
+        const int ch = (cc0 + cc) * 4 + g4;
         const bf16x8 a =
             *reinterpret_cast<const bf16x8*>(ks + row * ROW_BYTES + ((ch ^ swz_k<CPR, C::SHARED>(row)) << 4));
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
           s[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][cc], s[rt][kb], 0, 0, 0);
+      }
+    }
+    if constexpr (C::SPLIT_S) {
+      // Every wave of the row slice now holds the partial scores of its share of d,
+      // laid out identically; sum them through the exchange area. The barrier waits
+      // for LDS only: the ring's loads stay in flight. The exchange area is rewritten
+      // only after the next tile's ring barrier, when every wave has read it.
+      f32x4* xs = reinterpret_cast<f32x4*>(smem + C::RING_BYTES);
+      constexpr int NV = RTW * KB;  // 16-byte vectors per lane
+#pragma unroll
+      for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) xs[(wave * 64 + lane) * NV + rt * KB + kb] = s[rt][kb];
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt((15 << 0) | (7 << 4) | (3 << 14));  // lgkmcnt(0) only
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int o = 1; o < NCW; ++o) {
+        const int other = rw * NCW + (cw + o) % NCW;
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) s[rt][kb] += xs[(other * 64 + lane) * NV + rt * KB + kb];
       }
     }
 

@@ -19,92 +19,133 @@ namespace gqa {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
-constexpr int kThreads = 256;
-constexpr int kHeadChunk = 16;  // query heads of one group handled per workgroup
-constexpr int kAbsorbCols = 64; // latent columns per absorb workgroup
-constexpr int kUpCols = 16;     // output columns per up-projection workgroup
+constexpr int kThreads = 256;   // four independent waves per workgroup
+constexpr int kMaxDc = 512;     // the latent width d_c
 
-// Workgroup (row set, column chunk): rows = up to 16 heads of group g for token
-// (b, t); each of the 256 lanes owns one latent column c and four of the heads.
-__global__ __launch_bounds__(kThreads) void absorb_q_kernel(LatentProjParams p) {
-  __shared__ float qs[kHeadChunk][128 + 1];
+// Both projections run on the matrix cores, one 16 x 16 output tile per wave
+// (v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of A and column l % 16 of B,
+// each at the eight reduction indices 8 (l / 16) .. + 7 of every 32-wide step, and
+// receives D rows 4 (l / 16) .. + 3 of column l % 16). A tile's 16 rows are 16
+// consecutive rows of one group: row r of group g is head g H/G + r % (H/G) of token
+// r / (H/G), so every row of a tile uses the same W[g]. All of a wave's loads are
+// independent and issued together.
+__device__ __forceinline__ size_t group_row(const LatentProjParams& p, int g, int r) {
   const int hpg = p.H / p.G;
-  const int n_hc = (hpg + kHeadChunk - 1) / kHeadChunk;
-  int x = blockIdx.x;
-  const int hc = x % n_hc;
-  x /= n_hc;
-  const int g = x % p.G;
-  const int bt = x / p.G;                       // b * q_len + t
-  const int h0 = g * hpg + hc * kHeadChunk;
-  const int nh = min(kHeadChunk, hpg - hc * kHeadChunk);
+  return (size_t)(r / hpg) * p.H + g * hpg + r % hpg;   // row of [B q_len H]
+}
+
+// q_lat[row, c0 .. c0 + 15] = sum_i q[row, i] W_UK[g][i, c]
+template <int D_H>
+__global__ __launch_bounds__(kThreads) void absorb_q_kernel(LatentProjParams p) {
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int R_g = p.B * p.q_len * (p.H / p.G);           // rows per group
+  const int n_rt = (R_g + 15) / 16;
+  const int tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  constexpr int NCT = kMaxDc / 16;                        // column tiles
+  if (tile >= p.G * n_rt * NCT) return;
+  const int ct = tile % NCT;
+  const int rt = (tile / NCT) % n_rt;
+  const int g = tile / (NCT * n_rt);
+  const int r = rt * 16 + l16;                            // this lane's A row
+  const int c = ct * 16 + l16;                            // this lane's B column
   const __bf16* q = static_cast<const __bf16*>(p.q);
-  for (int e = threadIdx.x; e < nh * p.d_h; e += kThreads) {
-    const int k = e / p.d_h, i = e - k * p.d_h;
-    qs[k][i] = (float)q[((size_t)bt * p.H + h0 + k) * p.d_h + i];
-  }
-  __syncthreads();
-  const int c = blockIdx.y * kAbsorbCols + (threadIdx.x % kAbsorbCols);
-  const int kq = threadIdx.x / kAbsorbCols;    // heads kq, kq + 4, kq + 8, kq + 12
-  const __bf16* w = static_cast<const __bf16*>(p.w_uk) + (size_t)g * p.d_h * p.d_c + c;
-  float acc[kHeadChunk / 4] = {};
-  for (int i = 0; i < p.d_h; ++i) {
-    const float wv = (float)w[(size_t)i * p.d_c];
+  const __bf16* w = static_cast<const __bf16*>(p.w_uk) + (size_t)g * D_H * kMaxDc + c;
+  constexpr int KS = D_H / 32;                            // reduction steps
+  bf16x8 a[KS], b[KS];
 #pragma unroll
-    for (int j = 0; j < kHeadChunk / 4; ++j) acc[j] = __builtin_fmaf(qs[kq + 4 * j][i], wv, acc[j]);
+  for (int ks = 0; ks < KS; ++ks) {
+    a[ks] = r < R_g ? *reinterpret_cast<const bf16x8*>(q + group_row(p, g, r) * D_H + ks * 32 + g4 * 8) : bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[ks][e] = w[(size_t)(ks * 32 + g4 * 8 + e) * kMaxDc];
   }
+  f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], b[ks], d, 0, 0, 0);
   __bf16* dst = static_cast<__bf16*>(p.q_lat);
 #pragma unroll
-  for (int j = 0; j < kHeadChunk / 4; ++j) {
-    const int k = kq + 4 * j;
-    if (k < nh) dst[((size_t)bt * p.H + h0 + k) * p.d_c + c] = (__bf16)acc[j];
+  for (int j = 0; j < 4; ++j) {
+    const int rr = rt * 16 + g4 * 4 + j;
+    if (rr < R_g) dst[group_row(p, g, rr) * kMaxDc + c] = (__bf16)d[j];
   }
 }
 
-// Workgroup (row set, output chunk): lane (k, i) of 16 x 16 computes output column
-// i of head k as a dot product over the d_c latent columns, 8 at a time.
+// out[row, i0 .. i0 + 15] = sum_c u[row, c] W_UV[g][i, c], with u rounded to bf16 for
+// the matrix cores (the output is bf16 as well)
+template <int D_H>
 __global__ __launch_bounds__(kThreads) void up_proj_kernel(LatentProjParams p) {
-  const int hpg = p.H / p.G;
-  const int n_hc = (hpg + kHeadChunk - 1) / kHeadChunk;
-  int x = blockIdx.x;
-  const int hc = x % n_hc;
-  x /= n_hc;
-  const int g = x % p.G;
-  const int bt = x / p.G;
-  const int k = threadIdx.x / kUpCols;
-  const int i = blockIdx.y * kUpCols + (threadIdx.x % kUpCols);
-  if (hc * kHeadChunk + k >= hpg) return;
-  const size_t row = (size_t)bt * p.H + g * hpg + hc * kHeadChunk + k;
-  const float* u = p.u + row * p.d_c;
-  const __bf16* w = static_cast<const __bf16*>(p.w_uv) + ((size_t)g * p.d_h + i) * p.d_c;
-  float acc0 = 0.f, acc1 = 0.f;
-  for (int c = 0; c < p.d_c; c += 8) {
-    const bf16x8 wv = *reinterpret_cast<const bf16x8*>(w + c);
-    const f32x4 u0 = *reinterpret_cast<const f32x4*>(u + c);
-    const f32x4 u1 = *reinterpret_cast<const f32x4*>(u + c + 4);
+  const int lane = threadIdx.x & 63;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int R_g = p.B * p.q_len * (p.H / p.G);
+  const int n_rt = (R_g + 15) / 16;
+  const int tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  constexpr int NOT = D_H / 16;                           // output tiles
+  if (tile >= p.G * n_rt * NOT) return;
+  const int ot = tile % NOT;
+  const int rt = (tile / NOT) % n_rt;
+  const int g = tile / (NOT * n_rt);
+  const int r = rt * 16 + l16;
+  const int i = ot * 16 + l16;
+  const float* u = p.u + (r < R_g ? group_row(p, g, r) : 0) * kMaxDc + g4 * 8;
+  const __bf16* w = static_cast<const __bf16*>(p.w_uv) + ((size_t)g * D_H + i) * kMaxDc + g4 * 8;
+  constexpr int KS = kMaxDc / 32;
+  f32x4 u0[KS], u1[KS];
+  bf16x8 b[KS];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc0 = __builtin_fmaf(u0[e], (float)wv[e], acc0);
-      acc1 = __builtin_fmaf(u1[e], (float)wv[4 + e], acc1);
+  for (int ks = 0; ks < KS; ++ks) {
+    if (r < R_g) {
+      u0[ks] = *reinterpret_cast<const f32x4*>(u + ks * 32);
+      u1[ks] = *reinterpret_cast<const f32x4*>(u + ks * 32 + 4);
+    } else {
+      u0[ks] = u1[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    b[ks] = *reinterpret_cast<const bf16x8*>(w + ks * 32);
   }
-  static_cast<__bf16*>(p.out)[row * p.d_h + i] = (__bf16)(acc0 + acc1);
+  f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8 a = {(__bf16)u0[ks][0], (__bf16)u0[ks][1], (__bf16)u0[ks][2], (__bf16)u0[ks][3],
+                      (__bf16)u1[ks][0], (__bf16)u1[ks][1], (__bf16)u1[ks][2], (__bf16)u1[ks][3]};
+    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[ks], d, 0, 0, 0);
+  }
+  __bf16* dst = static_cast<__bf16*>(p.out);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rr = rt * 16 + g4 * 4 + j;
+    if (rr < R_g) dst[group_row(p, g, rr) * D_H + i] = (__bf16)d[j];
+  }
 }
 
 }  // namespace
 
+// d_c must be 512 and d_h 64 or 128 (checked by the planner).
+static int tile_blocks(const LatentProjParams& p, int col_tiles) {
+  const int R_g = p.B * p.q_len * (p.H / p.G);
+  const long long tiles = (long long)p.G * ((R_g + 15) / 16) * col_tiles;
+  return (int)((tiles + kThreads / 64 - 1) / (kThreads / 64));
+}
+
 hipError_t launch_latent_absorb_q(const LatentProjParams& p, hipStream_t stream) {
-  const int n_hc = (p.H / p.G + kHeadChunk - 1) / kHeadChunk;
-  const dim3 grid(p.B * p.q_len * p.G * n_hc, p.d_c / kAbsorbCols);
-  hipLaunchKernelGGL(absorb_q_kernel, grid, dim3(kThreads), 0, stream, p);
+  if (p.d_c != kMaxDc || (p.d_h != 64 && p.d_h != 128)) return hipErrorInvalidValue;
+  const dim3 grid(tile_blocks(p, kMaxDc / 16));
+  if (p.d_h == 64)
+    hipLaunchKernelGGL(absorb_q_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(absorb_q_kernel<128>, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 hipError_t launch_latent_up_proj(const LatentProjParams& p, hipStream_t stream) {
-  const int n_hc = (p.H / p.G + kHeadChunk - 1) / kHeadChunk;
-  const dim3 grid(p.B * p.q_len * p.G * n_hc, p.d_h / kUpCols);
-  hipLaunchKernelGGL(up_proj_kernel, grid, dim3(kThreads), 0, stream, p);
+  if (p.d_c != kMaxDc || (p.d_h != 64 && p.d_h != 128)) return hipErrorInvalidValue;
+  const dim3 grid(tile_blocks(p, p.d_h / 16));
+  if (p.d_h == 64)
+    hipLaunchKernelGGL(up_proj_kernel<64>, grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(up_proj_kernel<128>, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -145,7 +145,9 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams p) {
   constexpr int LPR = D / 4;               // lanes per row (4 columns each)
   constexpr int NGRP = kThreads / LPR;     // partial groups
-  constexpr int U = 4;                     // partials in flight per lane
+  // partials in flight per lane: a 512-wide row leaves only two lane groups per
+  // workgroup, so each takes more at once
+  constexpr int U = D == 512 ? 16 : 4;
   __shared__ float sm_m[NGRP];
   __shared__ float sm_l[NGRP];
   __shared__ f32x4 sm_o[NGRP][LPR];
@@ -206,6 +208,9 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
 
   float m = kNegInf, l = 0.f;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // with at least as many tiles as workgroups every workgroup owns a tile, and the
+  // per-partial emptiness test (two 64-bit divisions) can be skipped
+  const bool all_owned = W >= p.nwg;
   for (int base = wa + grp; base <= wb; base += NGRP * U) {
     float lse[U];
     f32x4 v[U];
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
       const int w = base + u * NGRP;
       lse[u] = kNegInf;
       v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (w <= wb && tile_lo(w, W, p.nwg) < tile_lo(w + 1, W, p.nwg)) {  // else empty
+      if (w <= wb && (all_owned || tile_lo(w, W, p.nwg) < tile_lo(w + 1, W, p.nwg))) {  // else empty
         const size_t prow = ((size_t)w * kPersistSlots + (w == wa ? slot_a : 0)) * RB + r_local;
         lse[u] = p.ws_lse[prow];
         v[u] = *reinterpret_cast<const f32x4*>(p.ws_o + prow * D + c);
