@@ -320,7 +320,9 @@ def test_latent_plan(H, G, q_len, rows, blocks):
     n = B * q_len * H
     attn = up(100 * 2 * rb * 512 * 4) + up(100 * 2 * rb * 4) + up((B + 1) * 4)
     assert pl.workspace_bytes == up(n * 512 * 2) + up(n * 512 * 4) + attn
-    assert pl.lds_bytes == 2 * 32 * 512 * 2          # two stages of 32 latent rows, staged once
+    # two stages of 32 latent rows, staged once, and the 8 KiB where the waves add their
+    # partial QK^T scores
+    assert pl.lds_bytes == 2 * 32 * 512 * 2 + 8192
     size = ctypes.c_size_t(0)
     o = opts(num_splits=100)
     assert _lib.lib().gqla_absorb_workspace_size(B, H, G, 128, 512, q_len, ctypes.byref(o), ctypes.byref(size)) == OK
