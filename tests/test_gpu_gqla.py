@@ -166,3 +166,18 @@ def test_full_size_sampled_parity():
         e = assert_parity(host64(out[b:b + 1]), oracle_latent(inp, [b]), "bfloat16", f"{wl.name} b={b}")
         print(f"[gqla] {wl.name} b={b} L={int(inp.lens[b])}: max_abs {e['max_abs']:.2e} "
               f"rel_l2 {e['rel_l2']:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("splits", [0, 37])
+def test_many_sequences(splits):
+    """More than 64 sequences (several chunks of the schedule scan), ragged, paged."""
+    from gqa_kv_cache_03_amd import gqla_absorb_decode
+    rng = np.random.default_rng(4500)
+    lens = rng.integers(1, 200, size=100).astype(np.int32)
+    lens[70] = 1500
+    wl, lens = latent_workload(100, 16, 2, 128, 1, list(lens), paged=16, seed=4600)
+    inp = make_latent_inputs(wl, device="cuda", lens=lens)
+    out = gqla_absorb_decode(inp.q, inp.latent, inp.w_uk, inp.w_uv, inp.seq_lens, inp.block_table,
+                             scale=wl.scale, num_splits=splits)
+    torch.cuda.synchronize()
+    assert_parity(host64(out), oracle_latent(inp), "bfloat16", f"B=100 splits={splits}")

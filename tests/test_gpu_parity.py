@@ -274,3 +274,18 @@ def test_scale_argument_is_applied():
         out = gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, scale=s)
         torch.cuda.synchronize()
         assert_parity(host64(out), _oracle_scale(inp, s), "float32", f"scale={s}")
+
+
+@pytest.mark.parametrize("B,page", [(65, 0), (130, 16), (200, 0)])
+@pytest.mark.parametrize("splits", [0, 37])
+def test_many_sequences(B, page, splits):
+    """More than 64 sequences: the kernel's schedule scan and the merge's prefix sums
+    take several 64-lane chunks of seq_lens."""
+    rng = np.random.default_rng(5000 + B + page)
+    lens = rng.integers(1, 300, size=B).astype(np.int32)
+    lens[B // 2] = 2048                                   # one long sequence mid-batch
+    wl, lens = small_workload(B, 32, 8, 128, 1, list(lens), paged=page, seed=5100 + B)
+    inp = make(wl, lens)
+    print(f"[parity] many sequences B={B} page={page} splits={splits}", flush=True)
+    got = run(inp, num_splits=splits)
+    assert_parity(got, oracle_for(inp), "bfloat16", f"B={B} page={page} splits={splits}")
