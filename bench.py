@@ -351,8 +351,11 @@ def main():
             buf = torch.cat([k.view(torch.uint8).reshape(-1) for k in ks])
         nbytes = buf.numel() // 16 * 16
         sink = torch.empty(8192, dtype=torch.int32, device=dev)
+        # the direct-to-LDS method in the decode kernel's own step: a K + V tile, or a
+        # tile of the 512-wide latent
+        step = 32768 if latent else 16384
         for label, fn in (("register_loads", lambda: read_stream(buf[:nbytes], sink)),
-                          ("lds_double_buffer", lambda: read_stream(buf[:nbytes]))):
+                          ("lds_double_buffer", lambda: read_stream(buf[:nbytes], step_bytes=step))):
             fn()
             torch.cuda.synchronize()
             c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -130,7 +130,7 @@ def lib() -> ctypes.CDLL:
     L.gqa_abi_version.restype = i32
     L.gqa_bench_read_stream.argtypes = [vp, sz, vp, vp]
     L.gqa_bench_read_stream.restype = i32
-    L.gqa_bench_read_stream_lds.argtypes = [vp, sz, i32, vp]
+    L.gqa_bench_read_stream_lds.argtypes = [vp, sz, i32, i32, vp]
     L.gqa_bench_read_stream_lds.restype = i32
     L.gqla_absorb_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                      vp, ctypes.POINTER(DecodeOpts)]

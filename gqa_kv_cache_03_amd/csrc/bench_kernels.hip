@@ -48,10 +48,10 @@ __global__ __launch_bounds__(kThreads) void read_stream_kernel(const u32x4* __re
 }
 
 // The decode kernel's own streaming pattern without its compute: two persistent
-// workgroups per CU, each reading one contiguous share of the buffer in 16 KiB steps
-// of direct-to-LDS loads (four 16-byte loads per lane), one step in flight while the
-// wave issues the next. The LDS copies are not read.
-constexpr int kStepChunks = 4;  // 16-byte loads per lane per step
+// workgroups per CU, each reading one contiguous share of the buffer in steps of
+// direct-to-LDS loads (16 KiB = four 16-byte loads per lane, as a K + V tile of the
+// 128-wide kernels; 32 KiB = eight, as a tile of the 512-wide latent), one step in
+// flight while the wave issues the next. The LDS copies are not read.
 
 __device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* lds_wave_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -62,6 +62,7 @@ __device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* l
 #endif
 }
 
+template <int kStepChunks>  // 16-byte loads per lane per step
 __global__ __launch_bounds__(kThreads) void read_stream_lds_kernel(const unsigned char* __restrict__ buf, size_t n16) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2][kStepChunks * kThreads * 16];
   const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void read_stream_lds_kernel(const unsigne
       const size_t i = base + (size_t)u * kThreads + threadIdx.x;
       if (i < hi) dma16(buf + i * 16, &lds[stage][u * kThreads * 16 + wave * 1024]);
     }
-    // at most this step's loads stay in flight: vmcnt(4), expcnt and lgkmcnt untouched
+    // at most this step's loads stay in flight: vmcnt(kStepChunks), expcnt and lgkmcnt untouched
     __builtin_amdgcn_s_waitcnt((kStepChunks & 15) | (7 << 4) | (15 << 8));
     stage ^= 1;
   }
@@ -84,12 +85,19 @@ __global__ __launch_bounds__(kThreads) void read_stream_lds_kernel(const unsigne
 
 }  // namespace
 
-extern "C" int gqa_bench_read_stream_lds(const void* buf, size_t bytes, int workgroups, void* stream) {
+extern "C" int gqa_bench_read_stream_lds(const void* buf, size_t bytes, int workgroups, int step_bytes,
+                                         void* stream) {
   if (!buf || bytes == 0 || (bytes % 16) != 0 || workgroups <= 0 || workgroups > (1 << 20))
     return GQA_ERR_INVALID_ARGUMENT;
   if ((reinterpret_cast<uintptr_t>(buf) % 16) != 0) return GQA_ERR_INVALID_ARGUMENT;
-  hipLaunchKernelGGL(read_stream_lds_kernel, dim3(workgroups), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const unsigned char*>(buf), bytes / 16);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const unsigned char* b = static_cast<const unsigned char*>(buf);
+  if (step_bytes == 16384)
+    hipLaunchKernelGGL(read_stream_lds_kernel<4>, dim3(workgroups), dim3(kThreads), 0, s, b, bytes / 16);
+  else if (step_bytes == 32768)
+    hipLaunchKernelGGL(read_stream_lds_kernel<8>, dim3(workgroups), dim3(kThreads), 0, s, b, bytes / 16);
+  else
+    return GQA_ERR_INVALID_ARGUMENT;
   return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 

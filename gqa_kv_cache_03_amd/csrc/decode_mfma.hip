@@ -654,10 +654,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       // only after the next tile's ring barrier, when every wave has read it.
       f32x4* xs = reinterpret_cast<f32x4*>(smem + C::RING_BYTES);
       constexpr int NV = RTW * KB;  // 16-byte vectors per lane
+      // [wave][vector][lane]: each 16-byte store and load of a wave is contiguous
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) xs[(wave * 64 + lane) * NV + rt * KB + kb] = s[rt][kb];
+        for (int kb = 0; kb < KB; ++kb) xs[(wave * NV + rt * KB + kb) * 64 + lane] = s[rt][kb];
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_waitcnt((15 << 0) | (7 << 4) | (3 << 14));  // lgkmcnt(0) only
       __builtin_amdgcn_s_barrier();
@@ -668,7 +669,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) s[rt][kb] += xs[(other * 64 + lane) * NV + rt * KB + kb];
+          for (int kb = 0; kb < KB; ++kb) s[rt][kb] += xs[(other * NV + rt * KB + kb) * 64 + lane];
       }
     }
 

@@ -189,12 +189,13 @@ def workspace_bytes(q, k_cache, block_table=None, **kw) -> int:
     return plan(q, k_cache, block_table, **kw)["workspace_bytes"]
 
 
-def read_stream(buf, sink=None, workgroups: int = 0) -> None:
+def read_stream(buf, sink=None, workgroups: int = 0, step_bytes: int = 16384) -> None:
     """Measurement helper: stream-read `buf` (a device tensor) once.
 
     With `sink` (int32 device tensor of >= 8192 entries): wide nontemporal loads into
     registers. Without: the decode kernel's pattern, `workgroups` persistent workgroups
-    (0: two per CU) reading through direct-to-LDS double-buffered steps.
+    (0: two per CU) reading through direct-to-LDS double-buffered steps of `step_bytes`
+    (16384 or 32768).
     """
     import torch
     L = _lib.lib()
@@ -205,7 +206,7 @@ def read_stream(buf, sink=None, workgroups: int = 0) -> None:
     else:
         if workgroups <= 0:
             workgroups = 2 * torch.cuda.get_device_properties(buf.device).multi_processor_count
-        st = L.gqa_bench_read_stream_lds(buf.data_ptr(), nbytes, workgroups, stream)
+        st = L.gqa_bench_read_stream_lds(buf.data_ptr(), nbytes, workgroups, step_bytes, stream)
     if st != _lib.GQA_OK:
         raise GqaError(st, "gqa_bench_read_stream")
 

@@ -32,10 +32,12 @@ int gqa_bench_read_stream(const void* buf, size_t bytes, void* sink, void* strea
  * gqa_bench_read_stream_lds -- read `bytes` bytes at `buf` (16-byte aligned, a
  * multiple of 16) the way the decode kernel streams its cache, minus the compute:
  * `workgroups` persistent workgroups (the decode kernel uses two per CU) each read one
- * contiguous share in 16 KiB steps of direct-to-LDS loads, one step in flight.
- * Asynchronous on `stream`. Returns a gqa_status.
+ * contiguous share in steps of `step_bytes` (16384: a K + V tile of the 64/128-wide
+ * kernels; 32768: a tile of the 512-wide latent) of direct-to-LDS loads, one step in
+ * flight. Asynchronous on `stream`. Returns a gqa_status (INVALID_ARGUMENT for another
+ * step size).
  */
-int gqa_bench_read_stream_lds(const void* buf, size_t bytes, int workgroups, void* stream);
+int gqa_bench_read_stream_lds(const void* buf, size_t bytes, int workgroups, int step_bytes, void* stream);
 
 #pragma GCC visibility pop
 

@@ -207,9 +207,10 @@ def test_bench_helper_validation():
     assert L.gqa_bench_read_stream(None, 16, P, None) == INV
     assert L.gqa_bench_read_stream(P, 15, P, None) == INV
     assert L.gqa_bench_read_stream(P + 4, 16, P, None) == INV
-    assert L.gqa_bench_read_stream_lds(None, 16, 8, None) == INV
-    assert L.gqa_bench_read_stream_lds(P, 15, 8, None) == INV
-    assert L.gqa_bench_read_stream_lds(P, 16, 0, None) == INV
+    assert L.gqa_bench_read_stream_lds(None, 16, 8, 16384, None) == INV
+    assert L.gqa_bench_read_stream_lds(P, 15, 8, 16384, None) == INV
+    assert L.gqa_bench_read_stream_lds(P, 16, 0, 16384, None) == INV
+    assert L.gqa_bench_read_stream_lds(P, 16, 8, 8192, None) == INV
 
 
 def call_append(kn=P, vn=P, **kw):
