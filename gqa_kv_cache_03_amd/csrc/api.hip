@@ -20,6 +20,7 @@ using gqa::DecodeParams;
 
 constexpr int kMaxRows = 1024;        // packed rows per KV group (H/G * q_len)
 constexpr int kLatentWidth = 512;     // d_c of the GQLA latent (the kernel's head width)
+constexpr int kSplitBlockRows = 128;  // rows per block when a group needs several
 constexpr int kMaxMappedHeads = 256;  // query heads a head -> group map may cover
 constexpr int kTargetSlots = 8192;   // split-kernel workgroup slots the VALU heuristic aims for
 constexpr size_t kWsAlign = 256;
@@ -126,7 +127,14 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
     // with more packed rows than one workgroup holds is split into equal row blocks,
     // each a segment that reads the group's K/V (at that size the step is bound by the
     // matrix cores, not by the extra reads).
-    const int block_rows = gqa::mfma_max_rows(d_h);
+    // A group that needs more than one block is cut into blocks of at most 128 rows
+    // (for the 64/128-wide kernels): their variant leaves room for two workgroups per
+    // CU, which measured faster than half as many 256-row blocks. Each block reads the
+    // group's K/V once more, but the blocks of a group are neighbours in the schedule
+    // and stream the same tiles at about the same time, so the caches serve most of
+    // the repeats (four blocks of 512 rows: 1.13x the single-read bytes from HBM).
+    int block_rows = gqa::mfma_max_rows(d_h);
+    if (R > block_rows && d_h != kLatentWidth) block_rows = kSplitBlockRows;
     const int n_rb = (int)((R + block_rows - 1) / block_rows);
     const int rb_rows = n_rb == 1 ? (int)R : (int)(((R + n_rb - 1) / n_rb + 15) / 16 * 16);
     const long long max_tiles = (long long)B * G * n_rb * ((capacity + kMfmaTile - 1) / kMfmaTile);

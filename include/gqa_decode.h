@@ -110,7 +110,8 @@ typedef struct gqa_plan {
   int32_t row_blocks;         /* split-K grid: workgroups that share one (b, g, split)
                                  along rows; persistent: row blocks per KV group (a
                                  group of more than 256 packed rows is split into equal
-                                 blocks, each reading the group's K/V) */
+                                 blocks of at most 128, each reading the group's K/V;
+                                 the 512-wide latent: blocks of at most 32) */
   int32_t tile_tokens;        /* keys staged per pipeline step */
   int32_t chunk_tokens;       /* split-K grid: keys per context split; else 0 */
   int32_t max_splits;         /* split-K grid: ceil(capacity / chunk_tokens);

@@ -191,8 +191,8 @@ def test_every_row_count_up_to_the_maximum_plans(R):
     assert pl.policy == (_lib.GQA_POLICY_MFMA if R >= 4 else _lib.GQA_POLICY_VALU)
     assert pl.lds_bytes <= 160 * 1024
     if pl.policy == _lib.GQA_POLICY_MFMA:
-        # row blocks of at most 256 rows that together cover R
-        assert pl.row_blocks == -(-R // 256)
+        # one block up to 256 rows; a larger group in blocks of at most 128 rows
+        assert pl.row_blocks == (1 if R <= 256 else -(-R // 128))
 
 
 def test_status_strings():
@@ -235,12 +235,12 @@ def test_append_workspace_checked():
 
 
 def test_row_blocks_split_large_groups_evenly():
-    """R = 16 tokens x 32 heads = 512 rows: two blocks of 256; R = 300: two of 160;
-    the partial slots hold one block's rows."""
-    for q_len, H, rb_rows in ((16, 32, 256), (10, 30, 160)):
+    """R = 16 tokens x 32 heads = 512 rows: four blocks of 128; R = 300: three of 112
+    (100 rounded up to 16); the partial slots hold one block's rows."""
+    for q_len, H, rb_rows in ((16, 32, 128), (10, 30, 112)):
         st, pl = plan(B=2, H=H, G=1, q_len=q_len, o=opts(cache_capacity=4096, num_splits=64))
         R = H * q_len
-        assert st == OK and pl.row_blocks == -(-R // 256)
+        assert st == OK and pl.row_blocks == -(-R // 128)
         assert pl.row_blocks * rb_rows >= R and rb_rows % 16 == 0
         assert pl.workspace_bytes == ro(64 * 2 * rb_rows * 128 * 4) + ro(64 * 2 * rb_rows * 4) + ro(3 * 4)
 

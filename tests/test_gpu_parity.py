@@ -55,9 +55,9 @@ CASES = [
     (2, 24, 4, 128, 2, [100, 701], "bfloat16", 0),     # R = 12
     (2, 8, 2, 64, 2, [90, 260], "bfloat16", 0),        # d = 64 on MFMA
     (2, 32, 1, 64, 4, [90, 1000], "bfloat16", 16),     # d = 64, R = 128, paged
-    (1, 32, 1, 128, 16, [1500], "bfloat16", 0),        # R = 512: two row blocks of 256
-    (2, 30, 1, 128, 10, [900, 40], "bfloat16", 32),    # R = 300: two blocks of 160, paged 32
-    (2, 64, 1, 64, 9, [300, 50], "bfloat16", 0),       # R = 576: three blocks of 192, d = 64
+    (1, 32, 1, 128, 16, [1500], "bfloat16", 0),        # R = 512: four row blocks of 128
+    (2, 30, 1, 128, 10, [900, 40], "bfloat16", 32),    # R = 300: three blocks of 112, paged 32
+    (2, 64, 1, 64, 9, [300, 50], "bfloat16", 0),       # R = 576: five blocks of 128, d = 64
     (2, 32, 2, 128, 12, [700, 64], "bfloat16", 32),    # q_len 12, R = 192, paged 32
     (1, 32, 1, 128, 16, [600], "float32", 0),          # fp32, R = 512 on the vector ALUs
     (2, 16, 2, 64, 16, [300, 17], "float32", 32),      # fp32, q_len 16, paged 32, L ~ q_len
