@@ -868,12 +868,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 template <int D, int NRW, int NCW, int RTW>
 hipError_t launch_variant(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
+  static_assert(kThreads == 256, "launch_timed launches 256 threads");
   if (paged)
-    hipExtLaunchKernelGGL((decode_mfma_kernel<D, NRW, NCW, RTW, true>), grid, dim3(kThreads), 0, stream, start, stop,
-                          0, p);
+    launch_timed(decode_mfma_kernel<D, NRW, NCW, RTW, true>, grid, stream, start, stop, p);
   else
-    hipExtLaunchKernelGGL((decode_mfma_kernel<D, NRW, NCW, RTW, false>), grid, dim3(kThreads), 0, stream, start,
-                          stop, 0, p);
+    launch_timed(decode_mfma_kernel<D, NRW, NCW, RTW, false>, grid, stream, start, stop, p);
   return hipGetLastError();
 }
 

@@ -203,10 +203,9 @@ template <typename TT, int D, int RB>
 hipError_t launch3(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream, hipEvent_t start,
                    hipEvent_t stop) {
   if (paged)
-    hipExtLaunchKernelGGL((decode_valu_kernel<TT, D, RB, true>), grid, dim3(kThreads), 0, stream, start, stop, 0, p);
+    launch_timed(decode_valu_kernel<TT, D, RB, true>, grid, stream, start, stop, p);
   else
-    hipExtLaunchKernelGGL((decode_valu_kernel<TT, D, RB, false>), grid, dim3(kThreads), 0, stream, start, stop, 0,
-                          p);
+    launch_timed(decode_valu_kernel<TT, D, RB, false>, grid, stream, start, stop, p);
   return hipGetLastError();
 }
 

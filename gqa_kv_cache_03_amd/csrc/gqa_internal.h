@@ -44,6 +44,18 @@ struct DecodeParams {
 
 // Row r of the packed group tile is query token t = r / hpg of head g*hpg + r % hpg.
 
+// Launch `kernel` with the decode parameter block on `stream`. With a start or stop
+// event the launch stamps them with the kernel's own begin and end times
+// (hipExtLaunchKernel); without, it is a plain launch (also inside graph capture).
+template <typename K>
+inline void launch_timed(K kernel, dim3 grid, hipStream_t stream, hipEvent_t start, hipEvent_t stop,
+                         const DecodeParams& p) {
+  if (start || stop)
+    hipExtLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, start, stop, 0, p);
+  else
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, p);
+}
+
 // Launchers (defined next to their kernels). Return hipSuccess or the launch error.
 // `start` / `stop` (may be null) are caller-created events that the launch itself
 // stamps with the kernel's own begin and end times (hipExtLaunchKernel), so the

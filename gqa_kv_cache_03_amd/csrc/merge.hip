@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(DecodeParams p) {
 template <typename TT, int D>
 hipError_t go(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const int total = p.B * p.q_len * p.H;
-  hipExtLaunchKernelGGL((merge_kernel<TT, D>), dim3(total), dim3(kThreads), 0, stream, start, stop, 0, p);
+  launch_timed(merge_kernel<TT, D>, dim3(total), stream, start, stop, p);
   return hipGetLastError();
 }
 
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
 template <int D>
 hipError_t go_persistent(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   const dim3 grid(p.B * p.G * p.n_row_blocks * p.row_block);
-  hipExtLaunchKernelGGL((merge_persistent_kernel<D>), grid, dim3(kThreads), 0, stream, start, stop, 0, p);
+  launch_timed(merge_persistent_kernel<D>, grid, stream, start, stop, p);
   return hipGetLastError();
 }
 

@@ -1,0 +1,93 @@
+"""The library runs on the stream it is given and can be captured in a HIP graph.
+
+- A call issued on a side stream gives the same bits as one on the default stream
+  (the persistent schedule is deterministic: no atomics, a fixed combine order).
+- gqa_decode and gqla_absorb_decode captured once in a graph (workspace and output
+  allocated beforehand; the library allocates nothing and records no memset) give, on
+  every replay, the bits an eager call gives for the inputs current at that replay:
+  the queries are rewritten in place between replays, with eager work and
+  synchronisations in between.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from gpu_cases import make, small_workload  # noqa: E402
+from gqa_synth import Workload, make_latent_inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_kv_cache_03_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+@pytest.mark.parametrize("page", [0, 16])
+def test_side_stream_matches_default_stream(page):
+    from gqa_kv_cache_03_amd import gqa_decode
+    wl, lens = small_workload(3, 32, 8, 128, 2, [300, 2000, 77], paged=page, seed=6100 + page)
+    inp = make(wl, lens)
+    ref = gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table, scale=wl.scale)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table, scale=wl.scale)
+    s.synchronize()
+    assert torch.equal(got, ref)
+
+
+def test_graph_replays_gqa_decode():
+    from gqa_kv_cache_03_amd import gqa_decode, plan
+    wl, lens = small_workload(4, 32, 8, 128, 1, [900, 64, 3000, 1500], paged=16, seed=6200)
+    inp = make(wl, lens)
+    pl = plan(inp.q, inp.k_cache, inp.block_table)
+    ws = torch.empty(max(pl["workspace_bytes"], 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(inp.q)
+    kw = dict(scale=wl.scale, out=out, workspace=ws)
+    gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table, **kw)   # warm-up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table, **kw)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(6201)
+    for rep in range(4):
+        inp.q.copy_(torch.randn(inp.q.shape, generator=gen, device="cuda").to(inp.q.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table, scale=wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"replay {rep}"
+
+
+def test_graph_replays_gqla_absorb_decode():
+    from gqa_kv_cache_03_amd import gqla_absorb_decode, gqla_plan
+    wl = Workload(name="t_gqla_graph", B=3, H=16, G=2, d_h=128, q_len=1, dtype="bfloat16", len_lo=100,
+                  len_hi=1200, layout="paged", page_size=16, seed=6300, extra_pages=2, d_c=512)
+    inp = make_latent_inputs(wl, device="cuda", lens=np.array([100, 1200, 513], dtype=np.int32))
+    ws = torch.empty(gqla_plan(inp.q, inp.latent, inp.w_uk, inp.block_table)["workspace_bytes"],
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(inp.q)
+    args = (inp.q, inp.latent, inp.w_uk, inp.w_uv, inp.seq_lens, inp.block_table)
+    gqla_absorb_decode(*args, scale=wl.scale, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gqla_absorb_decode(*args, scale=wl.scale, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(6301)
+    for rep in range(3):
+        inp.q.copy_(torch.randn(inp.q.shape, generator=gen, device="cuda").to(inp.q.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = gqla_absorb_decode(*args, scale=wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"replay {rep}"
