@@ -408,6 +408,8 @@ def main():
         "read_ceiling_gbps": None if ceiling is None else round(ceiling, 1),
         "read_ceiling_by_method": ceilings or None,
         "kernel_ms": {"split_decode": round(dec_ms, 6), "lse_merge": round(mrg_ms, 6)},
+        # spread of the event-timed decode kernel over the K steps
+        "decode_ms_p10_p50_p90": [round(float(x), 6) for x in np.percentile(dec, [10, 50, 90])],
         "roofline": {
             "bound": "mfma" if mfma_bound else "hbm",
             "achieved": round(tflops, 2) if mfma_bound else round(achieved, 2),
