@@ -1,4 +1,5 @@
-// Host side of the C ABI: argument checks, launch planning and the two launches.
+// Host side of the C ABI: argument checks, launch planning and the launches (decode
+// and merge; for the GQLA absorbed path also the query fold and the up-projection).
 //
 // Every argument check runs before any HIP call, so invalid calls return a status
 // without touching the device. The library allocates nothing: split partials go to
@@ -127,7 +128,7 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
     // with more packed rows than one workgroup holds is split into equal row blocks,
     // each a segment that reads the group's K/V (at that size the step is bound by the
     // matrix cores, not by the extra reads).
-    // A group that needs more than one block is cut into blocks of at most 128 rows
+    // Such a group is cut into blocks of at most 128 rows
     // (for the 64/128-wide kernels): their variant leaves room for two workgroups per
     // CU, which measured faster than half as many 256-row blocks. Each block reads the
     // group's K/V once more, but the blocks of a group are neighbours in the schedule

@@ -18,8 +18,8 @@
 // them (flash-decoding split-K over context, with splits sized by work, not by length).
 //
 // Per workgroup: the group's R = (H/G) * q_len query rows are packed into 16-row MFMA
-// tiles held in registers (a group of more than 256 rows is split into row blocks,
-// each a segment of its own). K/V rows stream from HBM exactly once per row block (the
+// tiles held in registers (a group of more than 256 rows is split into row blocks of
+// at most 128, each a segment of its own). K/V rows stream from HBM exactly once per row block (the
 // aiwiki note after the listing: the cache is read once, not copied per head) through
 // a double-buffered LDS ring filled by direct global->LDS loads (nontemporal, 16 bytes
 // per lane); the ring keeps running across segment boundaries. Every packed row
@@ -28,7 +28,8 @@
 //
 // Options handled here as well: the cache append (the new tokens' rows come from
 // k_new / v_new and are copied into the cache from LDS), a call-time head -> KV head
-// map (non-uniform groups) and a per-(token, head) active mask.
+// map (non-uniform groups) and a per-(token, head) active mask. D = 512 is the GQLA
+// latent of the absorbed execution: one KV head that is both K and V, staged once.
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, A 16x32 / B 32x16 / C 16x16):
 //   S^T = K Q^T with K as the A operand (rows = keys) and Q^T as B (columns = query
@@ -37,7 +38,9 @@
 //   O^T = V^T P^T: A = V^T (one transposed LDS read per 4 keys x column), B = P^T in
 //   bf16, C = O^T with lane l holding output row l%16, so softmax rescales are per lane.
 // The four waves of a workgroup share each tile and split the rows (NRW) and the
-// output columns (NCW); every wave computes the scores it needs itself.
+// output columns (NCW); every wave computes the scores it needs itself, except at
+// D = 512, where the waves of a row slice split the scores' reduction over d and add
+// their parts through LDS.
 
 #include "gqa_internal.h"
 
