@@ -1,0 +1,96 @@
+"""Seeded random shapes against the fp64 oracle, GPU.
+
+Each case draws its sizes from a fixed seed, so the set is the same on every run:
+batch, heads, groups, head width, new tokens, ragged lengths, contiguous or paged
+(page 16 / 32 / 64 / 128), forced workgroup or split counts, causal or not, bf16 or
+fp32, either kernel policy.
+The point is to cross the plans' decision boundaries at combinations no hand-written
+case names: row blocks, policies, partial-slot layouts, page crossings and ragged
+tails, together.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from gpu_cases import assert_parity, host64, make, oracle_for, small_workload  # noqa: E402
+from gqa_synth import Workload, make_latent_inputs  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_kv_cache_03_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def draw_case(seed):
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    hpg = int(rng.choice([1, 2, 3, 4, 6, 8, 16, 32]))
+    H = G * hpg
+    q_len = int(rng.choice([1, 1, 1, 2, 3, 4, 8, 16]))
+    while hpg * q_len > 1024 or H > 256:
+        q_len = max(1, q_len // 2)
+        if hpg * q_len <= 1024 and H <= 256:
+            break
+        hpg = max(1, hpg // 2)
+        H = G * hpg
+    d = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 6))
+    lens = [int(rng.integers(q_len, 700)) for _ in range(B)]
+    page = int(rng.choice([0, 0, 16, 32, 64, 128]))
+    dtype = "float32" if rng.random() < 0.2 else "bfloat16"
+    causal = bool(rng.random() < 0.8)
+    splits = int(rng.choice([0, 0, 1, 2, 7, 50, 300]))
+    policy = str(rng.choice(["auto", "auto", "valu", "mfma"] if dtype == "bfloat16" else ["auto", "valu"]))
+    return B, H, G, d, q_len, lens, page, dtype, causal, splits, policy
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_gqa_shape(seed):
+    from gqa_kv_cache_03_amd import gqa_decode
+    B, H, G, d, q_len, lens, page, dtype, causal, splits, policy = draw_case(7000 + seed)
+    wl, lens = small_workload(B, H, G, d, q_len, lens, dtype=dtype, paged=page, seed=7100 + seed, causal=causal)
+    inp = make(wl, lens)
+    print(f"[random] seed={seed} B={B} H={H} G={G} d={d} q_len={q_len} page={page} {dtype} causal={causal} "
+          f"splits={splits} policy={policy} lens={list(lens)}", flush=True)
+    out = gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table, scale=wl.scale,
+                     causal=causal, num_splits=splits, policy=policy)
+    torch.cuda.synchronize()
+    assert_parity(host64(out), oracle_for(inp, causal=causal), dtype, f"seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_gqla_shape(seed):
+    from gqa_kv_cache_03_amd import gqla_absorb_decode
+    rng = np.random.default_rng(7500 + seed)
+    G = int(rng.choice([1, 2, 4]))
+    H = G * int(rng.choice([1, 4, 8]))
+    q_len = int(rng.choice([1, 1, 2, 3]))
+    B = int(rng.integers(1, 5))
+    d = int(rng.choice([64, 128]))
+    lens = np.array([int(rng.integers(q_len, 900)) for _ in range(B)], dtype=np.int32)
+    page = int(rng.choice([0, 16, 32]))
+    causal = bool(rng.random() < 0.8)
+    splits = int(rng.choice([0, 1, 9, 200]))
+    wl = Workload(name=f"t_rand_gqla_{seed}", B=B, H=H, G=G, d_h=d, q_len=q_len, dtype="bfloat16",
+                  len_lo=int(lens.min()), len_hi=int(lens.max()), layout="paged" if page else "contiguous",
+                  page_size=page, causal=causal, seed=7600 + seed, extra_pages=2 if page else 0, d_c=512)
+    inp = make_latent_inputs(wl, device="cuda", lens=lens)
+    print(f"[random gqla] seed={seed} B={B} H={H} G={G} d={d} q_len={q_len} page={page} causal={causal} "
+          f"splits={splits} lens={list(lens)}", flush=True)
+    out = gqla_absorb_decode(inp.q, inp.latent, inp.w_uk, inp.w_uv, inp.seq_lens, inp.block_table,
+                             scale=wl.scale, causal=causal, num_splits=splits)
+    torch.cuda.synchronize()
+    wk, wv = host64(inp.w_uk), host64(inp.w_uv)
+    if page:
+        tbl = inp.table.astype(np.int64)
+        ref = oracle.gqla_decode(host64(inp.q), host64(inp.latent), wk, wv, lens, wl.scale, block_table=tbl,
+                                 page_size=page, causal=causal)
+    else:
+        ref = oracle.gqla_decode(host64(inp.q), host64(inp.latent), wk, wv, lens, wl.scale, causal=causal)
+    assert_parity(host64(out), ref, "bfloat16", f"gqla seed {seed}")
