@@ -183,6 +183,7 @@ __device__ __forceinline__ void load16_to_lds(const unsigned char* src, unsigned
 // One column block: rows r (address a) and r + 16 (a + HI) of the same columns.
 template <int HI>
 __device__ __forceinline__ void lds_read_tr16_x2(unsigned a, bf16x4& lo, bf16x4& hi) {
+  static_assert(HI > 0 && HI < 65536, "LDS offset field");
 #if defined(__HIP_DEVICE_COMPILE__)
   u32x2 x, y;
   asm volatile(
@@ -204,6 +205,7 @@ __device__ __forceinline__ void lds_read_tr16_x2(unsigned a, bf16x4& lo, bf16x4&
 template <int HI>
 __device__ __forceinline__ void lds_read_tr16_x4(unsigned a, unsigned b, bf16x4& lo0, bf16x4& hi0,
                                                  bf16x4& lo1, bf16x4& hi1) {
+  static_assert(HI > 0 && HI < 65536, "LDS offset field");
 #if defined(__HIP_DEVICE_COMPILE__)
   u32x2 x0, y0, x1, y1;
   asm volatile(
@@ -223,6 +225,71 @@ __device__ __forceinline__ void lds_read_tr16_x4(unsigned a, unsigned b, bf16x4&
   (void)a;
   (void)b;
   lo0 = hi0 = lo1 = hi1 = bf16x4{};
+#endif
+}
+
+// Four column blocks at addresses a[0..3]: all eight reads, then one wait.
+template <int HI>
+__device__ __forceinline__ void lds_read_tr16_x8(const unsigned (&a)[4], u32x2 (&v)[4][2]) {
+  static_assert(HI > 0 && HI < 65536, "LDS offset field");
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[2][0]), "=&v"(v[2][1]),
+        "=&v"(v[3][0]), "=&v"(v[3][1])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(HI)
+      : "memory");
+#else
+  (void)a;
+  for (auto& x : v) x[0] = x[1] = u32x2{};
+#endif
+}
+
+// Plain 16-byte LDS reads of rows r (address a[i]) and r + 16 (a[i] + HI) for N
+// addresses, N = 2 or 4, all issued before one wait, for the same reason as the
+// transposed reads.
+template <int N, int HI>
+__device__ __forceinline__ void lds_read_b128_rows(const unsigned (&a)[N], u32x4 (&v)[N][2]) {
+  static_assert(N == 2 || N == 4, "two or four addresses");
+  static_assert(HI > 0 && HI < 65536, "LDS offset field");
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %4 offset:%6\n\t"
+        "ds_read_b128 %2, %5\n\t"
+        "ds_read_b128 %3, %5 offset:%6\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[1][0]), "=&v"(v[1][1])
+        : "v"(a[0]), "v"(a[1]), "i"(HI)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:%12\n\t"
+        "ds_read_b128 %2, %9\n\t"
+        "ds_read_b128 %3, %9 offset:%12\n\t"
+        "ds_read_b128 %4, %10\n\t"
+        "ds_read_b128 %5, %10 offset:%12\n\t"
+        "ds_read_b128 %6, %11\n\t"
+        "ds_read_b128 %7, %11 offset:%12\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[2][0]), "=&v"(v[2][1]),
+          "=&v"(v[3][0]), "=&v"(v[3][1])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(HI)
+        : "memory");
+  }
+#else
+  (void)a;
+  for (auto& x : v) x[0] = x[1] = u32x4{};
 #endif
 }
 
@@ -298,7 +365,7 @@ struct Cursor {
 template <int D, int NRW, int NCW, int RTW, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   using C = MfmaCfg<D, NRW, NCW, RTW>;
-  constexpr int T = C::T, NS = C::NS, AHEAD = C::AHEAD, KB = C::KB, CC = C::CC, CBW = C::CBW;
+  constexpr int T = C::T, NS = C::NS, AHEAD = C::AHEAD, KB = C::KB, CBW = C::CBW;
   constexpr int CPR = C::CPR, LOADS = C::LOADS, LD = C::LD, ROW_BYTES = C::ROW_BYTES;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
 
@@ -522,7 +589,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   bf16x8 qf[RTW][CCW];
   float m_run[RTW], l_run[RTW];
   f32x4 o[RTW][CBW];
-  int lim[RTW];
+  float neg_m[RTW];  // -m_run (0 while m_run = -inf)
+  int lim_k[RTW];    // the row's last visible key, less this lane's key offset g4 * 4
   int lim_min = 0;
   // query (token, head) of this lane's packed row in each row tile of the current
   // segment (-1: a padding row), and whether that pair is active
@@ -533,12 +601,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
       m_run[rt] = kNegInf;
+      neg_m[rt] = 0.f;
       l_run[rt] = 0.f;
 #pragma unroll
       for (int cb = 0; cb < CBW; ++cb) o[rt][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
       // padding rows take the last token's limit (their results are discarded)
       const int t = row_t[rt] >= 0 ? row_t[rt] : p.q_len - 1;
-      lim[rt] = p.causal ? (c.L - p.q_len + t) : (c.L - 1);  // last visible key
+      lim_k[rt] = (p.causal ? (c.L - p.q_len + t) : (c.L - 1)) - g4 * 4;
     }
     lim_min = p.causal ? (c.L - p.q_len) : (c.L - 1);
   };
@@ -629,26 +698,56 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   };
 
   // ---- 4. consume one staged tile: S^T = K Q^T, online softmax, O^T += V^T P^T ----
-  // masked: some key of the tile lies past a row's last visible key (only the last
-  // tile or two of a segment), so those logits are set to -inf first.
-  auto consume = [&](const unsigned char* ks, const unsigned char* vs, const int tile0, const bool masked) {
+  // Every LDS read address of a tile is one of the lane constants below (for ring
+  // stage 0) plus the stage's byte offset, one add per address per tile.
+  constexpr int HI = 16 * ROW_BYTES;  // 16 rows on (the staging swizzles repeat every 16 rows)
+  // QK^T A operands: key rows l16 and l16 + 16, chunk (cc0 + cc) * 4 + g4
+  unsigned k_lane[CCW];
+#pragma unroll
+  for (int cc = 0; cc < CCW; ++cc)
+    k_lane[cc] = lds_addr(smem + l16 * ROW_BYTES + ((((cc0 + cc) * 4 + g4) ^ swz_k<CPR, C::SHARED>(l16)) << 4));
+  // O^T += V^T P^T over this wave's output columns. k-slots 8 * g4 + e are keys
+  // 4 * g4 + e of block 0 (e < 4), then of block 1 (e >= 4); a V^T fragment (4 keys of
+  // one column per lane) is one transposed LDS read: lane p of a 16-lane group points
+  // at key row g4 * 4 + p / 4, columns c0 + 4 (p % 4) .. +3 of column block cb (the
+  // second half of the k-slots: the same columns 16 rows further on). In the latent
+  // the V tile is the K tile.
+  unsigned v_lane[CBW];
+#pragma unroll
+  for (int cb = 0; cb < CBW; ++cb) {
+    const int r = g4 * 4 + (l16 >> 2);
+    const int c = (cw * CBW + cb) * 16 + ((l16 & 3) << 2);
+    v_lane[cb] = lds_addr(smem + (C::SHARED ? 0 : C::TENSOR_BYTES) + r * ROW_BYTES +
+                          ((((c >> 3) ^ swz_v<CPR, C::SHARED>(r)) << 4) | ((c & 7) << 1)));
+  }
+
+  // so: the stage's byte offset. masked: some key of the tile lies past a row's last
+  // visible key (only the last tile or two of a segment), so those logits are set to
+  // -inf first.
+  auto consume = [&](const unsigned so, const int tile0, const bool masked) {
     f32x4 s[RTW][KB];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) s[rt][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K fragments in groups of up to four k-steps, one LDS round trip per group
+    constexpr int KG = CCW >= 4 ? 4 : CCW;
+    static_assert((KG == 2 || KG == 4) && CCW % KG == 0, "K read groups");
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int row = kb * 16 + l16;
+    for (int c0 = 0; c0 < CCW; c0 += KG) {
+      u32x4 kf[KG][KB];
+      unsigned ka[KG];
 #pragma unroll
-      for (int cc = 0; cc < CCW; ++cc) {
-        const int ch = (cc0 + cc) * 4 + g4;
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(ks + row * ROW_BYTES + ((ch ^ swz_k<CPR, C::SHARED>(row)) << 4));
+      for (int i = 0; i < KG; ++i) ka[i] = k_lane[c0 + i] + so;
+      lds_read_b128_rows<KG, HI>(ka, kf);
 #pragma unroll
-        for (int rt = 0; rt < RTW; ++rt)
-          s[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][cc], s[rt][kb], 0, 0, 0);
-      }
+      for (int i = 0; i < KG; ++i)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int rt = 0; rt < RTW; ++rt)
+            s[rt][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[i][kb]),
+                                                                qf[rt][c0 + i], s[rt][kb], 0, 0, 0);
     }
     if constexpr (C::SPLIT_S) {
       // Every wave of the row slice now holds the partial scores of its share of d,
@@ -676,14 +775,46 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       }
     }
 
+    // With separate K and V tiles, every V^T fragment is read right after the QK^T
+    // products are issued, so that the reads' latency passes while the matrix cores
+    // work; the scheduling barriers keep the products above the reads and the softmax
+    // below them. (The latent's wider rows would need twice the registers; it reads
+    // each pair of blocks just before its product.)
+    constexpr bool EARLY_V = !C::SHARED;
+    bf16x4 vlo[EARLY_V ? CBW : 1], vhi[EARLY_V ? CBW : 1];
+    if constexpr (EARLY_V) {
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (CBW >= 4) {
+        static_assert(CBW % 4 == 0, "V^T read groups");
+#pragma unroll
+        for (int c0 = 0; c0 < CBW; c0 += 4) {
+          const unsigned va[4] = {v_lane[c0] + so, v_lane[c0 + 1] + so, v_lane[c0 + 2] + so, v_lane[c0 + 3] + so};
+          u32x2 vf[4][2];
+          lds_read_tr16_x8<HI>(va, vf);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vlo[c0 + i] = __builtin_bit_cast(bf16x4, vf[i][0]);
+            vhi[c0 + i] = __builtin_bit_cast(bf16x4, vf[i][1]);
+          }
+        }
+      } else if constexpr (CBW == 2) {
+        lds_read_tr16_x4<HI>(v_lane[0] + so, v_lane[1] + so, vlo[0], vhi[0], vlo[1], vhi[1]);
+      } else {
+        lds_read_tr16_x2<HI>(v_lane[0] + so, vlo[0], vhi[0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
     // Online softmax (base 2). Logits are s * c with c = |scale| log2(e) > 0 (a
     // negative scale was moved into the query's sign), so the row max is taken on the
     // raw products and p = exp2(fma(s, c, -m)) costs one FMA per score. A row's
     // reference max m only moves when a tile max exceeds it by more than
     // 2^kRescaleLog2; until then p <= 2^kRescaleLog2 and O and l keep their scale, so
-    // most tiles skip the rescale (numerator and denominator share m). P is rounded to
-    // bf16 for the PV product and the denominator sums those rounded weights (dot2
-    // with (1, 1)), so the normalised weights sum to one.
+    // most tiles skip the rescale (numerator and denominator share m). Each lane first
+    // checks its own scores; only when one of them crosses that line anywhere in the
+    // wave are the row maxima formed across lanes. P is rounded to bf16 for the PV
+    // product and the denominator sums those rounded weights (dot2 with (1, 1)), so the
+    // normalised weights sum to one.
     bf16x2 pk[RTW][KB][2];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
@@ -691,54 +822,43 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         // a real (uniform) branch: without the empty volatile statement the compiler
         // turns the block into a compare and select per score on every tile
         asm volatile("");
+        const int d = lim_k[rt] - tile0;  // key kb * 16 + g4 * 4 + i is visible iff kb * 16 + i <= d
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (tile0 + kb * 16 + g4 * 4 + i > lim[rt]) s[rt][kb][i] = kNegInf;
+            if (kb * 16 + i > d) s[rt][kb][i] = kNegInf;
       }
       float mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rt][kb][i]);
-      mx = wave_max_across_groups(mx) * qk_c;
-      const bool grow = mx > m_run[rt] + kRescaleLog2;  // -inf + c = -inf: a first finite max grows
-      if (__builtin_amdgcn_ballot_w64(grow)) {
+      // -inf + c = -inf: a first finite max grows
+      if (__builtin_amdgcn_ballot_w64(mx * qk_c > m_run[rt] + kRescaleLog2)) {
+        mx = wave_max_across_groups(mx) * qk_c;
+        const bool grow = mx > m_run[rt] + kRescaleLog2;
         const float m_new = grow ? mx : m_run[rt];
         const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[rt] - m_new) : 1.f;
         l_run[rt] *= alpha;
 #pragma unroll
         for (int cb = 0; cb < CBW; ++cb) o[rt][cb] *= alpha;
         m_run[rt] = m_new;
+        neg_m[rt] = (m_new == kNegInf) ? 0.f : -m_new;
       }
-      const float neg_m = (m_run[rt] == kNegInf) ? 0.f : -m_run[rt];
       float sum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const bf16x2 e = {(__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][kb][2 * h], qk_c, neg_m)),
-                            (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][kb][2 * h + 1], qk_c, neg_m))};
+          const bf16x2 e = {(__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][kb][2 * h], qk_c, neg_m[rt])),
+                            (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][kb][2 * h + 1], qk_c, neg_m[rt]))};
           pk[rt][kb][h] = e;
           sum = __builtin_amdgcn_fdot2_f32_bf16(e, kOnes2, sum, false);
         }
       l_run[rt] += sum;
     }
 
-    // O^T += V^T P^T over this wave's output columns. k-slots 8 * g4 + e are keys
-    // 4 * g4 + e of block 0 (e < 4), then of block 1 (e >= 4); a V^T fragment (4 keys of
-    // one column per lane) is one transposed LDS read: lane p of a 16-lane group points
-    // at key row base + p / 4, columns c0 + 4 (p % 4) .. +3.
-    // LDS address of this lane's V^T fragment for column block cb (rows g4 * 4 ..;
-    // the second half of the k-slots is the same columns 16 rows further on, with the
-    // same swizzle)
-    auto vt_addr = [&](int cb) -> unsigned {
-      const int c0 = (cw * CBW + cb) * 16;
-      const int r = g4 * 4 + (l16 >> 2);
-      const int c = c0 + ((l16 & 3) << 2);
-      return lds_addr(vs + r * ROW_BYTES + ((((c >> 3) ^ swz_v<CPR, C::SHARED>(r)) << 4) | ((c & 7) << 1)));
-    };
     bf16x8 pb[RTW];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt) {
@@ -746,18 +866,20 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       const bf16x4 hi4 = __builtin_shufflevector(pk[rt][1][0], pk[rt][1][1], 0, 1, 2, 3);
       pb[rt] = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
     }
-    constexpr int HI = 16 * ROW_BYTES;
     auto pv = [&](int cb, bf16x4 lo4, bf16x4 hi4) {
       const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
       for (int rt = 0; rt < RTW; ++rt)
         o[rt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], o[rt][cb], 0, 0, 0);
     };
-    if constexpr (CBW % 2 == 0) {
+    if constexpr (EARLY_V) {
+#pragma unroll
+      for (int cb = 0; cb < CBW; ++cb) pv(cb, vlo[cb], vhi[cb]);
+    } else if constexpr (CBW % 2 == 0) {
 #pragma unroll
       for (int cb = 0; cb < CBW; cb += 2) {
         bf16x4 l0, h0, l1, h1;
-        lds_read_tr16_x4<HI>(vt_addr(cb), vt_addr(cb + 1), l0, h0, l1, h1);
+        lds_read_tr16_x4<HI>(v_lane[cb] + so, v_lane[cb + 1] + so, l0, h0, l1, h1);
         pv(cb, l0, h0);
         pv(cb + 1, l1, h1);
       }
@@ -765,7 +887,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
       for (int cb = 0; cb < CBW; ++cb) {
         bf16x4 l0, h0;
-        lds_read_tr16_x2<HI>(vt_addr(cb), l0, h0);
+        lds_read_tr16_x2<HI>(v_lane[cb] + so, l0, h0);
         pv(cb, l0, h0);
       }
     }
@@ -855,9 +977,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       issue_tile(issue, f + AHEAD);
       advance(issue);
     }
-    const unsigned char* ks = smem + (f % NS) * C::STAGE_BYTES;
     const int tile0 = cons.t * T;
-    consume(ks, C::SHARED ? ks : ks + C::TENSOR_BYTES, tile0, tile0 + T - 1 > lim_min);
+    const bool masked = tile0 + T - 1 > lim_min;
+    consume((unsigned)((f & 1) * C::STAGE_BYTES), tile0, masked);
     const bool seg_end = cons.t == cons.n - 1;
     if (seg_end || f == count - 1) {
       const bool complete = seg_from_start && seg_end;
