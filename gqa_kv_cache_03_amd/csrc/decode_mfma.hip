@@ -979,7 +979,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     }
     const int tile0 = cons.t * T;
     const bool masked = tile0 + T - 1 > lim_min;
-    consume((unsigned)((f & 1) * C::STAGE_BYTES), tile0, masked);
+    consume((unsigned)((f % NS) * C::STAGE_BYTES), tile0, masked);
     const bool seg_end = cons.t == cons.n - 1;
     if (seg_end || f == count - 1) {
       const bool complete = seg_from_start && seg_end;
