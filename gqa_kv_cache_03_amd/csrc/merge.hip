@@ -21,8 +21,9 @@
 // by workgroup boundaries left one partial per workgroup it touches: in the
 // workgroup's slot 0 if the segment holds the workgroup's first tile, else in
 // slot 1 (it is then that workgroup's last segment). The merge recomputes the same
-// ownership from the prefix sums the decode kernel published. One workgroup per
-// (segment, packed row).
+// ownership from the prefix sums the decode kernel published. One wave per (segment,
+// packed row), four rows per workgroup; with a call-time head map (whose rows are found
+// with a workgroup-wide ballot) or 512-wide rows, one workgroup per (segment, row).
 
 #include "gqa_internal.h"
 
@@ -266,8 +267,112 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
     put4<__bf16>(static_cast<__bf16*>(p.out) + orow * D + c, tot * inv);
 }
 
+// The same merge with one wave per (segment, packed row) and four rows of a segment
+// per workgroup, for contiguous head groups and D <= 128: the wave's 256 / D lane
+// groups take the row's partials in turn and combine through lane swaps, with no LDS
+// and no workgroup barrier.
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_persistent_wave_kernel(DecodeParams p) {
+  constexpr int LPR = D / 4;   // lanes per row group (4 columns each)
+  constexpr int NG = 64 / LPR; // row groups per wave
+  constexpr int U = 4;         // partials in flight per lane
+  static_assert(NG >= 2 && NG * LPR == 64, "a wave holds whole row groups");
+
+  const int RB = p.row_block;
+  const int quads = (RB + 3) / 4;
+  const int GS = p.G * p.n_row_blocks;
+  const int seg = blockIdx.x / quads;
+  const int r_local = (blockIdx.x - seg * quads) * 4 + (int)(threadIdx.x >> 6);
+  if (r_local >= RB) return;  // the whole wave
+  const int b = seg / GS;
+  const int gs = seg - b * GS;
+  const int g = gs / p.n_row_blocks;
+  const int r = (gs - g * p.n_row_blocks) * RB + r_local;
+  const int n_g = p.hpg;
+  if (r >= n_g * p.q_len) return;
+  const int t = r / n_g;
+  const int h = g * n_g + (r - t * n_g);
+  const size_t orow = ((size_t)b * p.q_len + t) * p.H + h;
+  const bool on = p.head_active == nullptr || p.head_active[orow] != 0;
+
+  const int W = p.ws_prefix[p.B];
+  const int pre = p.ws_prefix[b];
+  const int n = (p.ws_prefix[b + 1] - pre) / GS;
+  if (n <= 0 || W <= 0) return;
+  const int s0 = pre + gs * n;
+  const int wa = tile_owner(s0, W, p.nwg);
+  const int wb = tile_owner(s0 + n - 1, W, p.nwg);
+  if (wa == wb) return;
+
+  const int lane = threadIdx.x & 63;
+  const int grp = lane / LPR;
+  const int c = (lane % LPR) * 4;
+  const int slot_a = tile_lo(wa, W, p.nwg) < s0 ? 1 : 0;
+  const bool all_owned = W >= p.nwg;
+  float m = kNegInf, l = 0.f;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int base = wa + grp; base <= wb; base += NG * U) {
+    float lse[U];
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int w = base + u * NG;
+      lse[u] = kNegInf;
+      v[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (w <= wb && (all_owned || tile_lo(w, W, p.nwg) < tile_lo(w + 1, W, p.nwg))) {
+        const size_t prow = ((size_t)w * kPersistSlots + (w == wa ? slot_a : 0)) * RB + r_local;
+        lse[u] = p.ws_lse[prow];
+        v[u] = *reinterpret_cast<const f32x4*>(p.ws_o + prow * D + c);
+      }
+    }
+    float mu = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mu = fmaxf(mu, lse[u]);
+    if (mu == kNegInf) continue;
+    const float sc = __builtin_amdgcn_exp2f(m - mu);
+    acc *= sc;
+    l *= sc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wt = __builtin_amdgcn_exp2f(lse[u] - mu);
+      acc += wt * v[u];
+      l += wt;
+    }
+    m = mu;
+  }
+  // combine the row groups: lanes LPR, 2 LPR, ... apart hold the same columns
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const float l2 = __shfl_xor(l, off);
+    f32x4 a2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a2[i] = __shfl_xor(acc[i], off);
+    const float M = fmaxf(m, m2);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    const float w1 = __builtin_amdgcn_exp2f(m - Mu);
+    const float w2 = __builtin_amdgcn_exp2f(m2 - Mu);
+    acc = acc * w1 + a2 * w2;
+    l = l * w1 + l2 * w2;
+    m = M;
+  }
+  if (grp != 0) return;
+  const float inv = (l > 0.f && on) ? 1.f / l : 0.f;
+  if (p.out_f32)
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow * D + c) = acc * inv;
+  else
+    put4<__bf16>(static_cast<__bf16*>(p.out) + orow * D + c, acc * inv);
+}
+
 template <int D>
 hipError_t go_persistent(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if constexpr (D <= 128) {
+    if (p.head_group == nullptr) {
+      const dim3 grid(p.B * p.G * p.n_row_blocks * ((p.row_block + 3) / 4));
+      launch_timed(merge_persistent_wave_kernel<D>, grid, stream, start, stop, p);
+      return hipGetLastError();
+    }
+  }
   const dim3 grid(p.B * p.G * p.n_row_blocks * p.row_block);
   launch_timed(merge_persistent_kernel<D>, grid, stream, start, stop, p);
   return hipGetLastError();
