@@ -22,8 +22,9 @@
 // workgroup's slot 0 if the segment holds the workgroup's first tile, else in
 // slot 1 (it is then that workgroup's last segment). The merge recomputes the same
 // ownership from the prefix sums the decode kernel published. One wave per (segment,
-// packed row), four rows per workgroup; with a call-time head map (whose rows are found
-// with a workgroup-wide ballot) or 512-wide rows, one workgroup per (segment, row).
+// packed row), four rows per workgroup, when segments hold few partials; else (and
+// with a call-time head map, whose rows are found with a workgroup-wide ballot, or
+// 512-wide rows) one workgroup per (segment, row).
 
 #include "gqa_internal.h"
 
@@ -367,7 +368,11 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_wave_kernel(DecodeP
 template <int D>
 hipError_t go_persistent(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   if constexpr (D <= 128) {
-    if (p.head_group == nullptr) {
+    // A wave takes 4 * (256 / D) partials per round, a workgroup four times as many:
+    // the wave form wins while segments average up to two of its rounds of partials
+    // (about nwg / segments each), the workgroup form beyond.
+    const long long segments = (long long)p.B * p.G * p.n_row_blocks;
+    if (p.head_group == nullptr && p.nwg <= 2 * (4 * (256 / D)) * segments) {
       const dim3 grid(p.B * p.G * p.n_row_blocks * ((p.row_block + 3) / 4));
       launch_timed(merge_persistent_wave_kernel<D>, grid, stream, start, stop, p);
       return hipGetLastError();
