@@ -289,3 +289,32 @@ def test_many_sequences(B, page, splits):
     print(f"[parity] many sequences B={B} page={page} splits={splits}", flush=True)
     got = run(inp, num_splits=splits)
     assert_parity(got, oracle_for(inp), "bfloat16", f"B={B} page={page} splits={splits}")
+
+
+# The persistent merge takes one of two forms: a wave per (segment, row) while
+# segments average at most 2 * 4 * (256 / d) partials (nwg <= 8 * (256 / d) * B * G *
+# row blocks), else a workgroup per (segment, row). Each case below lands in the form
+# named, with segments of a few to a few hundred partials.
+MERGE_FORM_CASES = [
+    # B, H, G, d, q_len, lens, nwg, form
+    (16, 32, 8, 128, 1, (300, 2600), 64, "wave"),
+    (16, 32, 8, 128, 1, (300, 2600), 1024, "wave"),
+    (4, 16, 4, 64, 2, (700, 3000), 512, "wave"),
+    (2, 32, 1, 128, 4, (9000, 12000), 512, "workgroup"),
+    (1, 8, 1, 128, 2, (5000, 5000), 300, "workgroup"),
+    (2, 16, 2, 64, 1, (4000, 9000), 700, "workgroup"),
+]
+
+
+@pytest.mark.parametrize("B,H,G,d,q_len,lens,nwg,form", MERGE_FORM_CASES)
+def test_merge_forms(B, H, G, d, q_len, lens, nwg, form):
+    R = H // G * q_len
+    n_rb = 1 if R <= 256 else -(-R // 128)
+    assert (nwg <= 8 * (256 // d) * B * G * n_rb) == (form == "wave")
+    rng = np.random.default_rng(5200 + B * H + nwg)
+    L = rng.integers(lens[0], lens[1] + 1, size=B).astype(np.int32)
+    wl, L = small_workload(B, H, G, d, q_len, list(L), seed=5300 + nwg)
+    inp = make(wl, L)
+    print(f"[parity] merge form {form}: B={B} H={H} G={G} d={d} q_len={q_len} nwg={nwg}", flush=True)
+    got = run(inp, num_splits=nwg)
+    assert_parity(got, oracle_for(inp), "bfloat16", f"{form} form nwg={nwg}")
