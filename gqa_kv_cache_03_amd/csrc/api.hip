@@ -1,5 +1,5 @@
 // Host side of the C ABI: argument checks, launch planning and the launches (decode
-// and merge; for the GQLA absorbed path also the query fold and the up-projection).
+// and merge; for the GQLA absorbed path also the query fold).
 //
 // Every argument check runs before any HIP call, so invalid calls return a status
 // without touching the device. The library allocates nothing: split partials go to
@@ -365,10 +365,7 @@ int latent_impl(const void* q, const void* latent, const void* w_uk, const void*
   gqa::LatentProjParams pp{};
   pp.q = q;
   pp.w_uk = w_uk;
-  pp.w_uv = w_uv;
   pp.q_lat = ws;
-  pp.u = reinterpret_cast<const float*>(ws + lp.q_lat_bytes);
-  pp.out = out;
   pp.B = B;
   pp.H = H;
   pp.G = G;
@@ -389,6 +386,11 @@ int latent_impl(const void* q, const void* latent, const void* w_uk, const void*
   dp.table = block_table;
   dp.out = ws + lp.q_lat_bytes;
   dp.out_f32 = 1;
+  // the merge applies each row's W_UV and writes `out`
+  dp.w_uv = w_uv;
+  dp.proj_out = out;
+  dp.proj_dh = d_h;
+  dp.proj_groups = G;
   set_workspace(dp, p, ws + lp.q_lat_bytes + lp.u_bytes);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -398,7 +400,6 @@ int latent_impl(const void* q, const void* latent, const void* w_uk, const void*
   if (gqa::launch_decode_mfma(dp, GQA_DTYPE_BF16, d_c, paged, grid, s, ev[0], ev[1]) != hipSuccess)
     return GQA_ERR_HIP;
   if (gqa::launch_merge_persistent(dp, d_c, s, nullptr, ev[2]) != hipSuccess) return GQA_ERR_HIP;
-  if (gqa::launch_latent_up_proj(pp, s) != hipSuccess) return GQA_ERR_HIP;
   return GQA_OK;
 }
 

@@ -40,6 +40,13 @@ struct DecodeParams {
   int nwg;                 // persistent workgroups (MFMA policy)
   float qk_scale_log2;     // scale * log2(e): logits in base-2 units
   int out_f32;             // write `out` as float32 instead of the input dtype (latent path)
+  // GQLA absorbed execution (D = 512 merge only; w_uv null otherwise): `out` holds the
+  // weighted latents u, and the merge also writes proj_out = W_UV[group] u, bf16
+  // [B, q_len, H, proj_dh], with H / proj_groups query heads per group
+  const void* w_uv;        // [proj_groups, proj_dh, 512] bf16
+  void* proj_out;
+  int proj_dh;
+  int proj_groups;
 };
 
 // Row r of the packed group tile is query token t = r / hpg of head g*hpg + r % hpg.
@@ -71,18 +78,15 @@ hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t s
 // Writes k_new / v_new into the cache rows of the new tokens (vector-ALU path).
 hipError_t launch_append(const DecodeParams& p, int elem_bytes, int d_h, bool paged, hipStream_t stream);
 
-// GQLA latent path: the per-group projections around the latent attention.
+// GQLA latent path: the query fold before the latent attention (the up-projection
+// after it runs inside the merge).
 struct LatentProjParams {
   const void* q;        // [rows, d_h] bf16, rows = B * q_len * H (row = (b q_len + t) H + h)
   const void* w_uk;     // [G, d_h, d_c] bf16
-  const void* w_uv;     // [G, d_h, d_c] bf16
   void* q_lat;          // [rows, d_c] bf16: q folded through its group's W_UK
-  const float* u;       // [rows, d_c] float32: attention-weighted latent
-  void* out;            // [rows, d_h] bf16
   int B, H, G, q_len, d_h, d_c;
 };
 hipError_t launch_latent_absorb_q(const LatentProjParams& p, hipStream_t stream);
-hipError_t launch_latent_up_proj(const LatentProjParams& p, hipStream_t stream);
 
 // Geometry of the MFMA kernel variants, chosen by packed row count R.
 struct MfmaVariant {

@@ -8,8 +8,9 @@
 // applied after the weighted sum over tokens. So the step is
 //   1. q_lat[h] = W_UK[g(h)]^T q[h]            (absorb_q_kernel, here)
 //   2. u[h] = softmax(scale q_lat[h] . c_j) c   (the matrix-core decode kernel, with
-//      the latent as a single KV head that is both K and V)
-//   3. out[h] = W_UV[g(h)] u[h]                 (up_proj_kernel, here)
+//      the latent as a single KV head that is both K and V, and its merge)
+//   3. out[h] = W_UV[g(h)] u[h]                 (at the end of that merge, one row per
+//      workgroup, from the merged u in LDS)
 // Steps 1 and 3 are small (rows x d_h x d_c multiply-adds per step, with rows =
 // B * q_len * H); step 2 streams the latent cache and dominates.
 
@@ -26,7 +27,7 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 constexpr int kThreads = 256;   // four independent waves per workgroup
 constexpr int kMaxDc = 512;     // the latent width d_c
 
-// Both projections run on the matrix cores, one 16 x 16 output tile per wave
+// The query fold runs on the matrix cores, one 16 x 16 output tile per wave
 // (v_mfma_f32_16x16x32_bf16: lane l supplies row l % 16 of A and column l % 16 of B,
 // each at the eight reduction indices 8 (l / 16) .. + 7 of every 32-wide step, and
 // receives D rows 4 (l / 16) .. + 3 of column l % 16). A tile's 16 rows are 16
@@ -74,52 +75,6 @@ __global__ __launch_bounds__(kThreads) void absorb_q_kernel(LatentProjParams p) 
   }
 }
 
-// out[row, i0 .. i0 + 15] = sum_c u[row, c] W_UV[g][i, c], with u rounded to bf16 for
-// the matrix cores (the output is bf16 as well)
-template <int D_H>
-__global__ __launch_bounds__(kThreads) void up_proj_kernel(LatentProjParams p) {
-  const int lane = threadIdx.x & 63;
-  const int l16 = lane & 15, g4 = lane >> 4;
-  const int R_g = p.B * p.q_len * (p.H / p.G);
-  const int n_rt = (R_g + 15) / 16;
-  const int tile = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  constexpr int NOT = D_H / 16;                           // output tiles
-  if (tile >= p.G * n_rt * NOT) return;
-  const int ot = tile % NOT;
-  const int rt = (tile / NOT) % n_rt;
-  const int g = tile / (NOT * n_rt);
-  const int r = rt * 16 + l16;
-  const int i = ot * 16 + l16;
-  const float* u = p.u + (r < R_g ? group_row(p, g, r) : 0) * kMaxDc + g4 * 8;
-  const __bf16* w = static_cast<const __bf16*>(p.w_uv) + ((size_t)g * D_H + i) * kMaxDc + g4 * 8;
-  constexpr int KS = kMaxDc / 32;
-  f32x4 u0[KS], u1[KS];
-  bf16x8 b[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    if (r < R_g) {
-      u0[ks] = *reinterpret_cast<const f32x4*>(u + ks * 32);
-      u1[ks] = *reinterpret_cast<const f32x4*>(u + ks * 32 + 4);
-    } else {
-      u0[ks] = u1[ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    b[ks] = *reinterpret_cast<const bf16x8*>(w + ks * 32);
-  }
-  f32x4 d = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const bf16x8 a = {(__bf16)u0[ks][0], (__bf16)u0[ks][1], (__bf16)u0[ks][2], (__bf16)u0[ks][3],
-                      (__bf16)u1[ks][0], (__bf16)u1[ks][1], (__bf16)u1[ks][2], (__bf16)u1[ks][3]};
-    d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[ks], d, 0, 0, 0);
-  }
-  __bf16* dst = static_cast<__bf16*>(p.out);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rr = rt * 16 + g4 * 4 + j;
-    if (rr < R_g) dst[group_row(p, g, rr) * D_H + i] = (__bf16)d[j];
-  }
-}
-
 }  // namespace
 
 // d_c must be 512 and d_h 64 or 128 (checked by the planner).
@@ -136,16 +91,6 @@ hipError_t launch_latent_absorb_q(const LatentProjParams& p, hipStream_t stream)
     hipLaunchKernelGGL(absorb_q_kernel<64>, grid, dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL(absorb_q_kernel<128>, grid, dim3(kThreads), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_latent_up_proj(const LatentProjParams& p, hipStream_t stream) {
-  if (p.d_c != kMaxDc || (p.d_h != 64 && p.d_h != 128)) return hipErrorInvalidValue;
-  const dim3 grid(tile_blocks(p, p.d_h / 16));
-  if (p.d_h == 64)
-    hipLaunchKernelGGL(up_proj_kernel<64>, grid, dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(up_proj_kernel<128>, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

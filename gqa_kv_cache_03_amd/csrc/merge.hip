@@ -139,6 +139,38 @@ __device__ __forceinline__ int tile_owner(int f, int W, int nwg) {
   return (int)((((long long)f + 1) * nwg - 1) / W);
 }
 
+// GQLA absorbed execution, after the merge of a row's weighted latent u (512 values
+// in sm_u): out[row, i] = sum_c W_UV[gq][i, c] u[c], gq the row's query group. Each
+// output takes 256 / proj_dh threads, each a contiguous share of the columns with four
+// partial sums, added across the threads by lane swaps.
+__device__ __forceinline__ void project_up(const DecodeParams& p, const float* sm_u, size_t orow, int h) {
+  typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+  const int tid = threadIdx.x;
+  const int dh = p.proj_dh;              // 64 or 128
+  const int tpo = kThreads / dh;         // threads per output: 4 or 2
+  const int i = tid / tpo;
+  const int part = tid % tpo;
+  const int cols = 512 / tpo;            // 128 or 256
+  const int gq = h / (p.H / p.proj_groups);
+  const __bf16* w = static_cast<const __bf16*>(p.w_uv) + ((size_t)gq * dh + i) * 512 + part * cols;
+  const float* u = sm_u + part * cols;
+  float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int cc = 0; cc < cols; cc += 8) {
+    const bf16x8 wv = *reinterpret_cast<const bf16x8*>(w + cc);
+    const f32x4 u0 = *reinterpret_cast<const f32x4*>(u + cc);
+    const f32x4 u1 = *reinterpret_cast<const f32x4*>(u + cc + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = __builtin_fmaf((float)wv[e], u0[e], a[e]);
+      a[e] = __builtin_fmaf((float)wv[4 + e], u1[e], a[e]);
+    }
+  }
+  float acc = (a[0] + a[1]) + (a[2] + a[3]);
+  for (int off = 1; off < tpo; off <<= 1) acc += __shfl_xor(acc, off);
+  if (part == 0) static_cast<__bf16*>(p.proj_out)[orow * dh + i] = (__bf16)acc;
+}
+
 // One workgroup per (segment, row): D/4 lanes cover the row's D columns and the
 // workgroup's 256 / (D/4) lane groups take the segment's partials in turn, several
 // in flight per lane, each group keeping a running max; the groups then combine
@@ -154,6 +186,8 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
   __shared__ float sm_l[NGRP];
   __shared__ f32x4 sm_o[NGRP][LPR];
   __shared__ unsigned long long sm_heads[kThreads / 64];
+  __shared__ __attribute__((aligned(16))) float sm_u[D == 512 ? D : 4];  // GQLA: the merged latent
+  const bool proj = D == 512 && p.w_uv != nullptr;
 
   const int RB = p.row_block;                     // rows per segment
   const int GS = p.G * p.n_row_blocks;            // segments per sequence
@@ -201,11 +235,21 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
   const int s0 = pre + gs * n;
   const int wa = tile_owner(s0, W, p.nwg);
   const int wb = tile_owner(s0 + n - 1, W, p.nwg);
-  if (wa == wb) return;  // written whole by one workgroup
-
   const int tid = threadIdx.x;
   const int grp = tid / LPR;
   const int c = (tid % LPR) * 4;
+  if (wa == wb) {  // written whole by one workgroup
+    if constexpr (D == 512) {
+      if (proj) {
+        if (grp == 0)
+          *reinterpret_cast<f32x4*>(sm_u + c) =
+              *reinterpret_cast<const f32x4*>(static_cast<const float*>(p.out) + orow * D + c);
+        __syncthreads();
+        project_up(p, sm_u, orow, h);
+      }
+    }
+    return;
+  }
   const int slot_a = tile_lo(wa, W, p.nwg) < s0 ? 1 : 0;
 
   float m = kNegInf, l = 0.f;
@@ -248,24 +292,33 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
   }
   sm_o[grp][tid % LPR] = acc;
   __syncthreads();
-  if (grp != 0) return;
-  float M = kNegInf;
+  if (grp == 0) {
+    float M = kNegInf;
 #pragma unroll
-  for (int k = 0; k < NGRP; ++k) M = fmaxf(M, sm_m[k]);
-  const float Mu = (M == kNegInf) ? 0.f : M;
-  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
-  float lt = 0.f;
+    for (int k = 0; k < NGRP; ++k) M = fmaxf(M, sm_m[k]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f};
+    float lt = 0.f;
 #pragma unroll
-  for (int k = 0; k < NGRP; ++k) {
-    const float wt = __builtin_amdgcn_exp2f(sm_m[k] - Mu);
-    tot += wt * sm_o[k][tid];
-    lt += wt * sm_l[k];
+    for (int k = 0; k < NGRP; ++k) {
+      const float wt = __builtin_amdgcn_exp2f(sm_m[k] - Mu);
+      tot += wt * sm_o[k][tid];
+      lt += wt * sm_l[k];
+    }
+    const float inv = (lt > 0.f && on) ? 1.f / lt : 0.f;
+    if (proj)
+      *reinterpret_cast<f32x4*>(sm_u + c) = tot * inv;
+    else if (p.out_f32)
+      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow * D + c) = tot * inv;
+    else
+      put4<__bf16>(static_cast<__bf16*>(p.out) + orow * D + c, tot * inv);
   }
-  const float inv = (lt > 0.f && on) ? 1.f / lt : 0.f;
-  if (p.out_f32)
-    *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + orow * D + c) = tot * inv;
-  else
-    put4<__bf16>(static_cast<__bf16*>(p.out) + orow * D + c, tot * inv);
+  if constexpr (D == 512) {
+    if (proj) {
+      __syncthreads();
+      project_up(p, sm_u, orow, h);
+    }
+  }
 }
 
 // The same merge with one wave per (segment, packed row) and four rows of a segment

@@ -58,9 +58,10 @@ extern "C" {
  *                NULL.
  *
  * The workspace (gqla_absorb_workspace_size, always > 0) holds the absorbed queries
- * (bf16), the weighted latents (fp32) and the attention kernel's split partials. Four
+ * (bf16), the weighted latents (fp32) and the attention kernel's split partials. Three
  * launches: fold the queries, attend over the latent (the matrix-core decode kernel with
- * one KV head that serves as both K and V), merge, project up.
+ * one KV head that serves as both K and V), then merge the partials and project each
+ * row up through its group's W_UV.
  *
  * Errors: INVALID_ARGUMENT for NULL or misaligned pointers, non-positive sizes,
  * H % G != 0, non-finite scale, a bad opts struct or paged geometry; UNSUPPORTED for
