@@ -19,12 +19,12 @@
 //
 // Per workgroup: the group's R = (H/G) * q_len query rows are packed into 16-row MFMA
 // tiles held in registers (a group of more than 256 rows is split into row blocks of
-// at most 128, each a segment of its own). K/V rows stream from HBM exactly once per row block (the
-// aiwiki note after the listing: the cache is read once, not copied per head) through
-// a double-buffered LDS ring filled by direct global->LDS loads (nontemporal, 16 bytes
-// per lane); the ring keeps running across segment boundaries. Every packed row
-// consumes each staged tile, i.e. the H/G-fold broadcast happens in registers, never
-// in memory.
+// at most 128, each a segment of its own). K/V rows stream from HBM exactly once per
+// row block (the aiwiki note after the listing: the cache is read once, not copied per
+// head) through a double-buffered LDS ring filled by direct global->LDS loads
+// (nontemporal, 16 bytes per lane); the ring keeps running across segment boundaries.
+// Every packed row consumes each staged tile, i.e. the H/G-fold broadcast happens in
+// registers, never in memory.
 //
 // Options handled here as well: the cache append (the new tokens' rows come from
 // k_new / v_new and are copied into the cache from LDS), a call-time head -> KV head
@@ -382,10 +382,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   // Tiles per segment of sequence b: n_b = ceil(L_b / T). A KV group's R packed rows
   // form n_row_blocks blocks of at most row_block rows (one block unless R exceeds
   // what a workgroup's registers hold); each block is a segment of its own that reads
-  // the group's K/V. The GS = G * n_row_blocks segments of b are consecutive. Every wave scans seq_lens (a few hundred bytes) on its own, with
-  // cross-lane operations only (no LDS, no barrier), to find the total W and the
-  // segment holding its workgroup's first tile; the first wave of workgroup 0 also
-  // publishes the per-sequence prefix sums for the merge kernel.
+  // the group's K/V. The GS = G * n_row_blocks segments of b are consecutive. Every
+  // wave scans seq_lens (a few hundred bytes) on its own, with cross-lane operations
+  // only (no LDS, no barrier), to find the total W and the segment holding its
+  // workgroup's first tile; the first wave of workgroup 0 also publishes the
+  // per-sequence prefix sums for the merge kernel.
   const int L0 = lane < p.B ? clamp_len(p.seq_lens[lane], p.capacity) : 0;
   int total = wave_sum_i32(L0 > 0 ? (L0 + T - 1) / T : 0);
   for (int b0 = 64; b0 < p.B; b0 += 64) {
