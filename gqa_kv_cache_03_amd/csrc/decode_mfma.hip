@@ -357,9 +357,14 @@ struct MfmaCfg {
 };
 
 // Position in the flattened tile sequence: segment (b, g, rb) -- row block rb of KV
-// group g of sequence b -- tile t of n, sequence length L.
+// group g of sequence b -- tile t of n, sequence length L. Set per segment for the
+// staging: fast = the number of leading tiles the plain staging path takes (tiles
+// wholly before the end that hold no new token), and base = the byte offset of the
+// segment's row 0 in a contiguous cache.
 struct Cursor {
   int b, g, rb, t, n, L;
+  int fast;
+  uint64_t base;
 };
 
 template <int D, int NRW, int NCW, int RTW, bool PAGED>
@@ -436,6 +441,17 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     issue.rb = seg - issue.g * p.n_row_blocks;
     issue.t = (lo - pre_start) - seg * issue.n;
   }
+  const unsigned char* __restrict__ kn = static_cast<const unsigned char*>(p.k_new);
+  const unsigned char* __restrict__ vn = static_cast<const unsigned char*>(p.v_new);
+  auto seg_setup = [&](Cursor& c) {
+    int fast = c.L / T;
+    // with the append, tile t holds a new token (position >= L - q_len) iff
+    // t >= (L - q_len) / T (any t when L - q_len < T)
+    if (kn != nullptr) fast = min(fast, (c.L - p.q_len) / T);
+    c.fast = fast;
+    c.base = ((uint64_t)c.b * p.G + c.g) * (uint64_t)p.capacity * ROW_BYTES;
+  };
+  seg_setup(issue);
   Cursor cons = issue;
 
   auto advance = [&](Cursor& c) {
@@ -452,6 +468,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
           }
         }
       }
+      if (c.b < p.B) seg_setup(c);
     }
   };
 
@@ -464,8 +481,6 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   // Cache append (k_new set): positions new0 = L - q_len .. L - 1 are the new tokens,
   // read from k_new / v_new [B, q_len, G, D] instead of the cache (which does not
   // hold them yet); copy_new_rows writes them into the cache once they are in LDS.
-  const unsigned char* __restrict__ kn = static_cast<const unsigned char*>(p.k_new);
-  const unsigned char* __restrict__ vn = static_cast<const unsigned char*>(p.v_new);
   auto tile_has_new = [&](const Cursor& c) { return kn != nullptr && c.t * T + T > c.L - p.q_len; };
 
   auto cache_row = [&](const Cursor& c, const int* pg, int row, int j) -> size_t {
@@ -509,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     const bool has_new = tile_has_new(c);
     // A full tile (no row past the end, no new token) whose loads each stay within one
     // page: a scalar base per load plus the lane-constant offsets.
-    if (t0 + T <= end && !has_new && (!PAGED || (1 << pshift) >= C::RPL)) {
+    if (c.t < c.fast && (!PAGED || (1 << pshift) >= C::RPL)) {
 #pragma unroll
       for (int n = 0; n < LOADS; ++n) {
         const int j0 = t0 + n * C::RPL;  // first row of this load
@@ -519,7 +534,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
           page = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
           rb = (((size_t)page * p.G + c.g) * (size_t)(pmask + 1) + (j0 & pmask)) * ROW_BYTES;
         } else {
-          rb = (((size_t)c.b * p.G + c.g) * (size_t)p.capacity + j0) * ROW_BYTES;
+          rb = c.base + (uint64_t)(uint32_t)j0 * ROW_BYTES;
         }
         const int lds_off = n * kThreads * 16 + wave * 1024;  // this wave's 64 x 16 B slots
         load16_to_lds(kg + rb + koff[n % C::KP], st + lds_off);
