@@ -213,7 +213,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode step has no multi-GPU path in this build)", file=sys.stderr)
+              "(the decode step has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy_mib:
         calibrate_copy(args.calibrate_copy_mib)

@@ -3,7 +3,7 @@
  *
  * Not part of the attention method. The bandwidth-wall section of the llms.blog
  * GQA/MQA page says decode is bound by reloading the KV cache from HBM each step, so
- * the decode kernel is judged against what plain streaming reads achieve on the same
+ * the decode kernel is measured against what plain streaming reads achieve on the same
  * device; this helper measures that ceiling.
  */
 #ifndef GQA_BENCH_H
