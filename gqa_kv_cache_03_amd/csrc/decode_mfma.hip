@@ -741,6 +741,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   // visible key (only the last tile or two of a segment), so those logits are set to
   // -inf first.
   auto consume = [&](const unsigned so, const int tile0, const bool masked) {
+    // The two waves that share a SIMD (one per workgroup) alternate between matrix
+    // products and softmax; a wave issuing products and their operand reads runs at a
+    // raised issue priority (s_setprio 1), so the matrix cores are fed first while the
+    // other wave's softmax fills the gaps (2-4% faster at R = 128 and 512, neutral below).
+    __builtin_amdgcn_s_setprio(1);
     f32x4 s[RTW][KB];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
@@ -820,6 +825,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
 
     // Online softmax (base 2). Logits are s * c with c = |scale| log2(e) > 0 (a
     // negative scale was moved into the query's sign), so the row max is taken on the
@@ -889,8 +895,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         o[rt][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[rt], o[rt][cb], 0, 0, 0);
     };
     if constexpr (EARLY_V) {
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int cb = 0; cb < CBW; ++cb) pv(cb, vlo[cb], vhi[cb]);
+      __builtin_amdgcn_s_setprio(0);
     } else if constexpr (CBW % 2 == 0) {
 #pragma unroll
       for (int cb = 0; cb < CBW; cb += 2) {
