@@ -66,6 +66,8 @@ CASES = [
     (2, 8, 2, 128, 2, [77, 300], "float32", 0),         # fp32 -> vector-ALU path
     (2, 4, 1, 64, 3, [40, 129], "float32", 16),         # fp32, paged
     (1, 32, 1, 128, 16, [700], "bfloat16", 32),         # R = 512: two row blocks, paged 32
+    (2, 32, 8, 128, 16, [40, 16], "bfloat16", 0),       # new rows span two tiles; all rows new
+    (2, 16, 4, 128, 8, [70, 33], "bfloat16", 16),       # new rows across a tile and a page edge
 ]
 
 
