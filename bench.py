@@ -3,6 +3,11 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--append]
 
+With no --workload the step runs on the largest configuration that fits one GPU (the
+group sweep at G = 32: 8 sequences of 131072 + 4 tokens, 17.2 GB of K/V), and the line
+also carries `per_config`: the same measurement on the other long-context
+configurations (ragged, paged, and the group sweep at G = 1, 2, 4, 8).
+
 A step is one gqa_decode call (gqa_decode_append with --append; gqla_absorb_decode for
 a GQLA workload) over the whole batch of the workload, inputs resident in HBM. Several
 copies of the cache are rotated so that every step reads cold data (the 256 MiB
@@ -76,6 +81,8 @@ def parse():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="default run only: skip the other long-context configurations")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -209,28 +216,24 @@ def cpu_baseline_latent(inp, budget_s: float):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode step has no multi-GPU path)", file=sys.stderr)
-        sys.exit(2)
-    if args.calibrate_copy_mib:
-        calibrate_copy(args.calibrate_copy_mib)
-        return
+def measure(name, args, dev, variant_opts=True, ceiling=False):
+    """Generate workload `name` on `dev`, run args.warmup untimed steps, then time
+    exactly args.steps back-to-back steps; then time the decode and merge kernels with
+    the events their launches stamp over a second pass of the same steps. Returns the
+    measurements, the inputs and the plan."""
     import numpy as np
     import torch
 
     from gqa_kv_cache_03_amd import gqa_decode, gqa_decode_append, gqla_absorb_decode, gqla_plan, plan, read_stream
-    from gqa_synth import BENCH_DEFAULT, make_inputs, make_latent_inputs, workload
+    from gqa_synth import make_inputs, make_latent_inputs, workload
 
-    name = args.workload or BENCH_DEFAULT
     wl = workload(name)
     latent = bool(wl.d_c)   # a GQLA layer, run in its absorbed form
-    if latent and (args.append or args.head_map or args.active_frac > 0 or args.policy == "valu"):
+    use_append = args.append and variant_opts
+    head_map = args.head_map and variant_opts
+    active_frac = args.active_frac if variant_opts else 0.0
+    if latent and (use_append or head_map or active_frac > 0 or args.policy == "valu"):
         sys.exit("the GQLA absorbed path takes no --append, --head-map, --active-frac or valu policy")
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
     print(f"[bench] generating {name}", file=sys.stderr, flush=True)
     if latent:
         inp = make_latent_inputs(wl, device=dev)
@@ -247,7 +250,7 @@ def main():
     vs = [] if latent else [caches[1]] + [caches[1].clone() for _ in range(copies - 1)]
     out = torch.empty_like(inp.q)
     variant = {}
-    if args.head_map:
+    if head_map:
         # every KV head keeps at least one query head; the rest are dealt at random with
         # at most twice the uniform group size per KV head
         rng = np.random.default_rng(wl.seed + 7)
@@ -259,9 +262,9 @@ def main():
                 break
         variant["head_group"] = torch.as_tensor(m.astype(np.int32), device=dev)
         variant["max_group_heads"] = 2 * hpg
-    if args.active_frac > 0:
+    if active_frac > 0:
         rng = np.random.default_rng(wl.seed + 8)
-        act = (rng.random((wl.B, wl.q_len, wl.H)) < args.active_frac).astype(np.uint8)
+        act = (rng.random((wl.B, wl.q_len, wl.H)) < active_frac).astype(np.uint8)
         variant["head_active"] = torch.as_tensor(act, device=dev)
     if latent:
         kw = dict(scale=wl.scale, causal=wl.causal, num_splits=args.num_splits, policy=args.policy)
@@ -275,7 +278,7 @@ def main():
     ws = torch.empty(max(pl["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
 
     new_bytes = 0
-    if args.append:
+    if use_append:
         # the new tokens' rows, as the projections would hand them over: [B, q_len, G, d_h]
         k_new = torch.empty((wl.B, wl.q_len, wl.G, wl.d_h), dtype=inp.q.dtype, device=dev)
         v_new = torch.empty_like(k_new)
@@ -293,7 +296,7 @@ def main():
         if latent:
             gqla_absorb_decode(inp.q, ks[i % copies], inp.w_uk, inp.w_uv, inp.seq_lens, inp.block_table,
                                out=out, workspace=ws, profile_events=events, **kw)
-        elif args.append:
+        elif use_append:
             gqa_decode_append(inp.q, k_new, v_new, ks[i % copies], vs[i % copies], inp.seq_lens,
                               inp.block_table, out=out, workspace=ws, profile_events=events, **kw)
         else:
@@ -315,7 +318,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] {args.steps} steps: {ms * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us)",
+    print(f"[bench] {name}: {args.steps} steps, {ms * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us)",
           file=sys.stderr, flush=True)
 
     # per-kernel durations: the library's launches stamp these events with each kernel's own
@@ -341,9 +344,8 @@ def main():
     dec_alg_bytes = kv_bytes + q_bytes + tbl_bytes + new_bytes
     achieved = dec_alg_bytes / (dec_ms * 1e-3) / 1e9
 
-    ceiling = None
     ceilings = {}
-    if not args.no_ceiling:
+    if ceiling:
         # streaming-read ceiling over the same cache copies: wide register loads, and the
         # decode kernel's own direct-to-LDS pattern without its compute; the best counts
         buf = ks[0].view(torch.uint8).reshape(-1)
@@ -353,9 +355,9 @@ def main():
         sink = torch.empty(8192, dtype=torch.int32, device=dev)
         # the direct-to-LDS method in the decode kernel's own step: a K + V tile, or a
         # tile of the 512-wide latent
-        step = 32768 if latent else 16384
+        step_bytes = 32768 if latent else 16384
         for label, fn in (("register_loads", lambda: read_stream(buf[:nbytes], sink)),
-                          ("lds_double_buffer", lambda: read_stream(buf[:nbytes], step_bytes=step))):
+                          ("lds_double_buffer", lambda: read_stream(buf[:nbytes], step_bytes=step_bytes))):
             fn()
             torch.cuda.synchronize()
             c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -368,10 +370,8 @@ def main():
             c1.record()
             torch.cuda.synchronize()
             ceilings[label] = round(nbytes / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9, 1)
-        ceiling = max(ceilings.values())
         del buf
 
-    value = kv_bytes / (ms * 1e-3) / 1e9
     # useful matrix work of the decode kernel: QK^T and PV, 2 * 2 * d_h flop per
     # (query row, visible key) -- counted over all L keys (the causal triangle among
     # the q_len new tokens is a negligible correction)
@@ -381,6 +381,71 @@ def main():
     intensity = flops / dec_alg_bytes
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
     mfma_bound = pl["policy"] == "mfma" and intensity > ridge
+    del ks, vs, ws, out
+    return dict(wl=wl, inp=inp, pl=pl, latent=latent, variant=variant, copies=copies, ms=ms, wall=wall,
+                dec=dec, dec_ms=dec_ms, mrg_ms=mrg_ms, kv_bytes=kv_bytes, dec_alg_bytes=dec_alg_bytes,
+                achieved=achieved, flops=flops, tflops=tflops, intensity=intensity, mfma_bound=mfma_bound,
+                ceilings=ceilings)
+
+
+def roofline_of(m, traffic_key):
+    """The dominant (decode) kernel against the roofline that bounds it."""
+    mb = m["mfma_bound"]
+    return {
+        "bound": "mfma" if mb else "hbm",
+        "achieved": round(m["tflops"], 2) if mb else round(m["achieved"], 2),
+        "peak": MFMA_BF16_PEAK_TFLOPS if mb else HBM_PEAK_GBPS,
+        "unit": "TFLOP/s" if mb else "GB/s",
+        "frac": round(m["tflops"] / MFMA_BF16_PEAK_TFLOPS if mb else m["achieved"] / HBM_PEAK_GBPS, 4),
+        "traffic": load_traffic(traffic_key) if not m["variant"] else None,
+        "kernel": "decode_mfma_kernel" if m["pl"]["policy"] == "mfma" else "decode_valu_kernel",
+        "algorithmic_bytes_per_launch": int(m["dec_alg_bytes"]),
+        "flops_per_launch": int(m["flops"]),
+        "flop_per_byte": round(m["intensity"], 2),
+        "hbm_gbps": round(m["achieved"], 2),
+    }
+
+
+def per_config_entry(m):
+    """One long-context configuration's line in the default run."""
+    value = m["kv_bytes"] / (m["ms"] * 1e-3) / 1e9
+    r = roofline_of(m, m["wl"].name)
+    return {
+        "step_us": round(m["ms"] * 1e3, 2),
+        "kv_gbps": round(value, 1),
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(m["wl"].B * m["wl"].q_len / (m["ms"] * 1e-3), 1),
+        "decode_us": round(m["dec_ms"] * 1e3, 2),
+        "merge_us": round(m["mrg_ms"] * 1e3, 2),
+        "decode_roofline_frac": r["frac"],
+        "roofline_bound": r["bound"],
+        "traffic": r["traffic"],
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the decode step has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy_mib:
+        calibrate_copy(args.calibrate_copy_mib)
+        return
+    import numpy as np
+    import torch
+
+    from gqa_synth import BENCH_DEFAULT, BENCH_PER_CONFIG
+
+    name = args.workload or BENCH_DEFAULT
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    m = measure(name, args, dev, ceiling=not args.no_ceiling)
+    wl, inp, pl = m["wl"], m["inp"], m["pl"]
+    latent = m["latent"]
+    ms = m["ms"]
+    value = m["kv_bytes"] / (ms * 1e-3) / 1e9
+    ceiling = max(m["ceilings"].values()) if m["ceilings"] else None
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -401,36 +466,37 @@ def main():
             "B": wl.B, "H": wl.H, "G": wl.G, "d_h": wl.d_h, "q_len": wl.q_len, "d_c": wl.d_c or None,
             "layout": wl.layout, "page_size": wl.page_size or None,
             "lengths": [wl.len_lo, wl.len_hi], "sum_seq_lens": int(inp.lens.sum()),
-            "kv_bytes": int(kv_bytes), "kv_copies_rotated": copies, "plan": pl,
+            "kv_bytes": int(m["kv_bytes"]), "kv_copies_rotated": m["copies"], "plan": pl,
         },
         "tokens_per_s": round(wl.B * wl.q_len / (ms * 1e-3), 1),
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "read_ceiling_gbps": None if ceiling is None else round(ceiling, 1),
-        "read_ceiling_by_method": ceilings or None,
-        "kernel_ms": {"split_decode": round(dec_ms, 6), "lse_merge": round(mrg_ms, 6)},
+        "read_ceiling_by_method": m["ceilings"] or None,
+        "kernel_ms": {"split_decode": round(m["dec_ms"], 6), "lse_merge": round(m["mrg_ms"], 6)},
         # spread of the event-timed decode kernel over the K steps
-        "decode_ms_p10_p50_p90": [round(float(x), 6) for x in np.percentile(dec, [10, 50, 90])],
-        "roofline": {
-            "bound": "mfma" if mfma_bound else "hbm",
-            "achieved": round(tflops, 2) if mfma_bound else round(achieved, 2),
-            "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
-            "unit": "TFLOP/s" if mfma_bound else "GB/s",
-            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS if mfma_bound else achieved / HBM_PEAK_GBPS, 4),
-            "traffic": load_traffic(name + ("_append" if args.append else "")) if not variant else None,
-            "kernel": "decode_mfma_kernel" if pl["policy"] == "mfma" else "decode_valu_kernel",
-            "algorithmic_bytes_per_launch": int(dec_alg_bytes),
-            "flops_per_launch": int(flops),
-            "flop_per_byte": round(intensity, 2),
-            "hbm_gbps": round(achieved, 2),
-        },
-        "mfma_util": None if pl["policy"] != "mfma" else round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "decode_ms_p10_p50_p90": [round(float(x), 6) for x in np.percentile(m["dec"], [10, 50, 90])],
+        "roofline": roofline_of(m, name + ("_append" if args.append else "")),
+        "mfma_util": None if pl["policy"] != "mfma" else round(m["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
         "cpu_baseline": None,
-        "wall_ms_per_step": round(wall * 1e3 / args.steps, 6),
+        "per_config": None,
+        "wall_ms_per_step": round(m["wall"] * 1e3 / args.steps, 6),
     }
-    del ks, vs
+    del m
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline_latent(inp, args.cpu_budget) if latent else cpu_baseline(inp, args.cpu_budget)
+    del inp
+    torch.cuda.empty_cache()
+    if args.workload is None and not args.no_per_config:
+        # the default run also measures every other long-context configuration, with
+        # the same warm-up and step counts; plain calls (no append or grouping variant)
+        res["per_config"] = {}
+        for other in BENCH_PER_CONFIG:
+            mo = measure(other, args, dev, variant_opts=False)
+            res["per_config"][other] = per_config_entry(mo)
+            del mo
+            torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
 

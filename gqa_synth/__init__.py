@@ -4,7 +4,7 @@ This package is shared by the GPU path's tests/benchmark and by the CPU oracle's
 tests. It holds shapes, seeds and random draws only -- none of the attention
 arithmetic (no logits, softmax or weighted sums live here).
 """
-from .workloads import Workload, WORKLOADS, BENCH_DEFAULT, workload
+from .workloads import Workload, WORKLOADS, BENCH_DEFAULT, BENCH_PER_CONFIG, workload
 from .generate import (
     draw_lengths,
     draw_key_scales,
@@ -19,6 +19,7 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "BENCH_DEFAULT",
+    "BENCH_PER_CONFIG",
     "workload",
     "draw_lengths",
     "draw_key_scales",

@@ -145,8 +145,20 @@ for _w in [
 ]:
     WORKLOADS[_w.name] = _w
 
-# The single-GPU benchmark's default line: the Llama-3-8B-like decode layer.
-BENCH_DEFAULT = "llama3_8b_decode_bf16_B16_H32_G8_d128_n4096"
+# The single-GPU benchmark's default line: the largest configuration that fits one GPU,
+# the group sweep's MHA end (G = 32, 17.2 GB of K/V).
+BENCH_DEFAULT = "causal4_bf16_B8_H32_G32_d128_n131072p4"
+
+# The long-context configurations the benchmark also reports in its default run, each
+# with its step time, KV GB/s and decode-kernel roofline fraction.
+BENCH_PER_CONFIG = (
+    "llama2_70b_ragged_bf16_B32_H64_G8_d128_n1k_32k",
+    "paged16_bf16_B64_H32_G4_d128_n8k_64k",
+    "causal4_bf16_B8_H32_G1_d128_n131072p4",
+    "causal4_bf16_B8_H32_G2_d128_n131072p4",
+    "causal4_bf16_B8_H32_G4_d128_n131072p4",
+    "causal4_bf16_B8_H32_G8_d128_n131072p4",
+)
 
 
 def workload(name: str) -> Workload:

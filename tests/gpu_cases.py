@@ -80,3 +80,79 @@ def small_workload(B, H, G, d, q_len, lens, dtype="bfloat16", paged=0, seed=7, c
 
 def make(wl, lens, device="cuda"):
     return make_inputs(wl, device=device, lens=lens)
+
+
+def host_workers() -> int:
+    """Host threads for oracle work: the CPUs this process may use, at most 16."""
+    import os
+    try:
+        n = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def sequence_kv_host(inp, b):
+    """K and V of sequence b as host tensors [G, L_b, d] in the input dtype (the paged
+    pool gathered through the block table on the device first)."""
+    import torch
+    wl = inp.wl
+    L = int(inp.lens[b])
+    if inp.block_table is None:
+        return inp.k_cache[b, :, :L].cpu(), inp.v_cache[b, :, :L].cpu()
+    P = wl.page_size
+    n = -(-L // P)
+    pages = torch.as_tensor(inp.table[b, :n].astype(np.int64), device=inp.k_cache.device)
+    k = inp.k_cache[pages].transpose(0, 1).reshape(wl.G, n * P, wl.d_h)[:, :L]
+    v = inp.v_cache[pages].transpose(0, 1).reshape(wl.G, n * P, wl.d_h)[:, :L]
+    return k.cpu(), v.cpu()
+
+
+def all_units_parity(inp, out, what: str, log=print) -> dict:
+    """Compare every output element of a decode call with the fp64 oracle, one
+    (sequence, KV group) unit at a time, units spread over host threads.
+
+    out is the device output [B, q_len, H, d]. Each unit hands the oracle exactly the
+    rows its group reads (K and V of that sequence and group, the group's query heads)
+    and checks the group's output slice with assert_parity. Returns the worst errors.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    wl = inp.wl
+    hpg = wl.H // wl.G
+    got_all = out.cpu()
+    q_all = inp.q.cpu()
+    worst = {"max_abs": 0.0, "max_rel": 0.0, "rel_l2": 0.0, "units": 0}
+
+    def one(b, g, k_b, v_b):
+        lens = inp.lens[b:b + 1]
+        q = q_all[b:b + 1, :, g * hpg:(g + 1) * hpg].double().numpy()
+        k = k_b[g].double().numpy()[None, None]
+        v = v_b[g].double().numpy()[None, None]
+        ref = oracle.gqa_decode(q, k, v, lens, wl.scale, 1, causal=wl.causal)[0]
+        got = got_all[b, :, g * hpg:(g + 1) * hpg].double().numpy()
+        return assert_parity(got, ref, wl.dtype, f"{what} unit (b={b}, g={g}, L={int(lens[0])})")
+
+    workers = host_workers()
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=workers) as ex:
+        pending = []
+        for b in range(wl.B):
+            k_b, v_b = sequence_kv_host(inp, b)
+            pending += [ex.submit(one, b, g, k_b, v_b) for g in range(wl.G)]
+            # bound the host copies held at once: drain when two sequences' units are queued
+            while len(pending) > max(2 * wl.G, workers):
+                e = pending.pop(0).result()
+                for key in ("max_abs", "max_rel", "rel_l2"):
+                    worst[key] = max(worst[key], e[key])
+                worst["units"] += 1
+            del k_b, v_b
+        for f in pending:
+            e = f.result()
+            for key in ("max_abs", "max_rel", "rel_l2"):
+                worst[key] = max(worst[key], e[key])
+            worst["units"] += 1
+    log(f"[parity] {what}: {worst['units']} units, max_abs {worst['max_abs']:.2e} "
+        f"max_rel {worst['max_rel']:.2e} rel_l2 {worst['rel_l2']:.2e} ({workers} host threads)")
+    return worst
