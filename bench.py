@@ -489,11 +489,16 @@ def main():
     del inp
     torch.cuda.empty_cache()
     if args.workload is None and not args.no_per_config:
-        # the default run also measures every other long-context configuration, with
-        # the same warm-up and step counts; plain calls (no append or grouping variant)
+        # the default run also measures every other long-context configuration with plain
+        # calls (no append or grouping variant)
+        # (at least 50 warm-up and 100 timed steps each, so that short runs still report
+        # settled clocks for these shorter steps)
         res["per_config"] = {}
+        pc_args = argparse.Namespace(**vars(args))
+        pc_args.warmup, pc_args.steps = max(args.warmup, 50), max(args.steps, 100)
+        res["per_config_protocol"] = {"warmup": pc_args.warmup, "steps": pc_args.steps}
         for other in BENCH_PER_CONFIG:
-            mo = measure(other, args, dev, variant_opts=False)
+            mo = measure(other, pc_args, dev, variant_opts=False)
             res["per_config"][other] = per_config_entry(mo)
             del mo
             torch.cuda.empty_cache()
