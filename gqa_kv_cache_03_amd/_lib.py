@@ -15,6 +15,10 @@ GQA_ERR_INVALID_ARGUMENT = 1
 GQA_ERR_UNSUPPORTED = 2
 GQA_ERR_WORKSPACE = 3
 GQA_ERR_HIP = 4
+GQA_ERR_SCRATCH = 5
+
+# fixed per-device scratch behind gqa_decode_noalloc (GQA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 65 << 20
 
 GQA_DTYPE_F32 = 0
 GQA_DTYPE_BF16 = 1
@@ -28,6 +32,7 @@ EXPORTED = (
     "gqa_decode_opts_init",
     "gqa_decode",
     "gqa_decode_append",
+    "gqa_decode_noalloc",
     "gqa_decode_plan",
     "gqa_decode_workspace_size",
     "gqa_status_string",
@@ -116,6 +121,9 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float,
                              vp, ctypes.POINTER(DecodeOpts)]
     L.gqa_decode.restype = i32
+    L.gqa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float,
+                                     vp, ctypes.POINTER(DecodeOpts)]
+    L.gqa_decode_noalloc.restype = i32
     L.gqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float,
                                     vp, ctypes.POINTER(DecodeOpts)]
     L.gqa_decode_append.restype = i32

@@ -3,8 +3,9 @@
 //
 // Every argument check runs before any HIP call, so invalid calls return a status
 // without touching the device. The library allocates nothing: split partials go to
-// the caller's workspace. The only state it keeps is a per-device cache of the CU
-// count (a read-only device property).
+// the caller's workspace, or, for the no-allocation entry point, to a fixed device
+// array that the code object brings. The only state it keeps is a per-device cache of
+// the CU count (a read-only device property) and of that array's device address.
 
 #include <atomic>
 #include <cmath>
@@ -51,6 +52,33 @@ int device_cus() {
   }
   cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+// Scratch of the no-allocation entry point: a file-scope device array, so the code
+// object's loader places one copy on every GPU the library runs on, held until the
+// process ends. In host code `scratch` only names the symbol; its device address comes
+// from hipGetSymbolAddress, once per device, and only that address is handed to
+// kernels.
+constexpr size_t kScratchBytes = GQA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// This device's copy of `scratch` (looked up on the first call on a device; nullptr
+// on failure, with the HIP error cleared).
+void* device_scratch() {
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* ptr = cache[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  cache[dev].store(ptr, std::memory_order_release);
+  return ptr;
 }
 
 struct Plan {
@@ -250,10 +278,12 @@ void set_workspace(DecodeParams& dp, const Plan& p, void* ws_base) {
 }
 
 // Shared by gqa_decode (k_new == v_new == nullptr) and gqa_decode_append.
+// use_scratch: the no-allocation entry point -- the plan's partials go to this
+// device's `scratch` instead of opts->workspace (which is not read).
 int decode_impl(const void* q, const void* k_new, const void* v_new, const void* k_cache,
                 const void* v_cache, const int32_t* seq_lens, const int32_t* block_table, void* out,
                 int B, int H, int G, int d_h, int q_len, float scale, void* stream,
-                const gqa_decode_opts* opts) {
+                const gqa_decode_opts* opts, bool use_scratch = false) {
   if (!q || !k_cache || !v_cache || !seq_lens || !out || !opts) return GQA_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(seq_lens, 4) || (block_table && !aligned(block_table, 4)))
@@ -265,12 +295,19 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const void*
   Plan p;
   int st = make_plan(B, H, G, d_h, q_len, opts, paged, /*query_device=*/false, &p);
   if (st != GQA_OK) return st;
+  // the device-free plan has the most workgroups the device plan can have on MI355X,
+  // so an oversize plan is refused here, before any HIP call
+  if (use_scratch && p.pub.workspace_bytes > kScratchBytes) return GQA_ERR_SCRATCH;
   st = make_plan(B, H, G, d_h, q_len, opts, paged, /*query_device=*/true, &p);
   if (st != GQA_OK) return st;
   const gqa_plan& pl = p.pub;
-  if (pl.workspace_bytes > 0) {
-    if (!opts->workspace || !aligned(opts->workspace, kWsAlign) ||
-        opts->workspace_bytes < pl.workspace_bytes)
+  void* workspace = opts->workspace;
+  if (use_scratch) {
+    if (pl.workspace_bytes > kScratchBytes) return GQA_ERR_SCRATCH;
+    workspace = nullptr;
+    if (pl.workspace_bytes > 0 && (workspace = device_scratch()) == nullptr) return GQA_ERR_HIP;
+  } else if (pl.workspace_bytes > 0) {
+    if (!workspace || !aligned(workspace, kWsAlign) || opts->workspace_bytes < pl.workspace_bytes)
       return GQA_ERR_WORKSPACE;
   }
 
@@ -284,7 +321,7 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const void*
   dp.seq_lens = seq_lens;
   dp.table = block_table;
   dp.out = out;
-  if (pl.workspace_bytes > 0) set_workspace(dp, p, opts->workspace);
+  if (pl.workspace_bytes > 0) set_workspace(dp, p, workspace);
   dp.hpg = opts->head_group ? 1 : H / G;  // unused with a head map (groups are counted)
   dp.head_group = opts->head_group;
   dp.head_active = opts->head_active;
@@ -425,6 +462,8 @@ const char* gqa_status_string(int status) {
     case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
     case GQA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case GQA_ERR_HIP: return "HIP runtime error";
+    case GQA_ERR_SCRATCH:
+      return "the plan needs more split partials than the no-allocation entry point's scratch holds";
     default: return "unknown status";
   }
 }
@@ -458,6 +497,13 @@ int gqa_decode(const void* q, const void* k_cache, const void* v_cache, const in
                float scale, void* stream, const gqa_decode_opts* opts) {
   return decode_impl(q, nullptr, nullptr, k_cache, v_cache, seq_lens, block_table, out, B, H, G, d_h,
                      q_len, scale, stream, opts);
+}
+
+int gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                       const int32_t* block_table, void* out, int B, int H, int G, int d_h, int q_len,
+                       float scale, void* stream, const gqa_decode_opts* opts) {
+  return decode_impl(q, nullptr, nullptr, k_cache, v_cache, seq_lens, block_table, out, B, H, G, d_h,
+                     q_len, scale, stream, opts, /*use_scratch=*/true);
 }
 
 int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -95,6 +95,20 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, block_table=None, *, scale: Option
                  max_group_heads=max_group_heads, head_active=head_active)
 
 
+def gqa_decode_noalloc(q, k_cache, v_cache, seq_lens, block_table=None, *, scale: Optional[float] = None,
+                       out=None, causal: bool = True, num_splits: int = 0, chunk_tokens: int = 0,
+                       policy: str = "auto", profile_events=None, head_group=None,
+                       max_group_heads: int = 0, head_active=None):
+    """gqa_decode through the no-allocation entry point: the split partials go to the
+    library's fixed per-device scratch array, not to a workspace. `out` must be given
+    by a caller that may not allocate (it is allocated here only when None). Calls
+    that overlap on one GPU race on the scratch."""
+    return _call(q, None, None, k_cache, v_cache, seq_lens, block_table, scale=scale, out=out,
+                 causal=causal, num_splits=num_splits, chunk_tokens=chunk_tokens, policy=policy,
+                 workspace=None, profile_events=profile_events, head_group=head_group,
+                 max_group_heads=max_group_heads, head_active=head_active, noalloc=True)
+
+
 def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table=None, *,
                       scale: Optional[float] = None, out=None, causal: bool = True, num_splits: int = 0,
                       chunk_tokens: int = 0, policy: str = "auto", workspace=None, profile_events=None,
@@ -113,7 +127,7 @@ def gqa_decode_append(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table=N
 
 def _call(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table, *, scale, out, causal, num_splits,
           chunk_tokens, policy, workspace, profile_events, head_group=None, max_group_heads=0,
-          head_active=None):
+          head_active=None, noalloc=False):
     import torch
     tensors = [("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("seq_lens", seq_lens)]
     if k_new is not None or v_new is not None:
@@ -156,9 +170,10 @@ def _call(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table, *, scale, ou
                   head_active=head_active, **geo)
     L = _lib.lib()
     need = ctypes.c_size_t(0)
-    st = L.gqa_decode_workspace_size(B, H, G, d, q_len, ctypes.byref(o), ctypes.byref(need))
-    if st != _lib.GQA_OK:
-        raise GqaError(st, "gqa_decode_workspace_size")
+    if not noalloc:
+        st = L.gqa_decode_workspace_size(B, H, G, d, q_len, ctypes.byref(o), ctypes.byref(need))
+        if st != _lib.GQA_OK:
+            raise GqaError(st, "gqa_decode_workspace_size")
     if need.value:
         if workspace is None or workspace.numel() * workspace.element_size() < need.value:
             workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
@@ -173,6 +188,13 @@ def _call(q, k_new, v_new, k_cache, v_cache, seq_lens, block_table, *, scale, ou
             o.profile_events[i] = ev
     stream = torch.cuda.current_stream(q.device).cuda_stream
     bt = None if block_table is None else block_table.data_ptr()
+    if noalloc:
+        st = L.gqa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                                  bt, out.data_ptr(), B, H, G, d, q_len, ctypes.c_float(scale), stream,
+                                  ctypes.byref(o))
+        if st != _lib.GQA_OK:
+            raise GqaError(st, "gqa_decode_noalloc")
+        return out
     if k_new is None:
         st = L.gqa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(), bt,
                           out.data_ptr(), B, H, G, d, q_len, ctypes.c_float(scale), stream, ctypes.byref(o))

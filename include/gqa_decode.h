@@ -26,7 +26,10 @@
  *    the ABI. Every argument check runs on the host before any HIP call.
  *  - Device arrays are row-major, contiguous, 16-byte aligned, owned by the caller.
  *  - The library never allocates memory; the only state it keeps between calls is a
- *    per-device cache of the compute-unit count.
+ *    per-device cache of the compute-unit count and of the device address of the
+ *    no-allocation entry point's scratch array (GQA_NOALLOC_SCRATCH_BYTES, which the
+ *    code object's loader places on each GPU the library runs on, held until the
+ *    process ends).
  */
 #ifndef GQA_DECODE_H
 #define GQA_DECODE_H
@@ -48,8 +51,14 @@ typedef enum gqa_status {
   GQA_ERR_INVALID_ARGUMENT = 1, /* a NULL/misaligned pointer, a bad size, H % G != 0 ... */
   GQA_ERR_UNSUPPORTED = 2,      /* valid but not compiled: d_h not 64/128, R > 1024, ... */
   GQA_ERR_WORKSPACE = 3,        /* the plan needs split-K scratch the caller did not give */
-  GQA_ERR_HIP = 4               /* a HIP launch or event call failed */
+  GQA_ERR_HIP = 4,              /* a HIP launch or event call failed */
+  GQA_ERR_SCRATCH = 5           /* gqa_decode_noalloc: the plan's partials exceed
+                                   GQA_NOALLOC_SCRATCH_BYTES */
 } gqa_status;
+
+/* Size of the fixed per-device scratch behind gqa_decode_noalloc (65 MiB): the split
+ * partials of up to 512 persistent workgroups x 128 packed rows at d_h = 128. */
+#define GQA_NOALLOC_SCRATCH_BYTES ((size_t)65 << 20)
 
 typedef enum gqa_dtype { GQA_DTYPE_F32 = 0, GQA_DTYPE_BF16 = 1 } gqa_dtype;
 
@@ -188,6 +197,29 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
                       void* v_cache, const int32_t* seq_lens, const int32_t* block_table,
                       void* out, int B, int H, int G, int d_h, int q_len, float scale,
                       void* stream, const gqa_decode_opts* opts);
+
+/*
+ * gqa_decode_noalloc -- gqa_decode without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Arguments, layouts and results are those of gqa_decode;
+ * opts->workspace and opts->workspace_bytes are not read. The split partials go to a
+ * fixed array of GQA_NOALLOC_SCRATCH_BYTES per GPU, owned by the library: the call
+ * itself allocates nothing and launches the same kernels as gqa_decode.
+ *
+ * Limit: plans whose workspace (gqa_decode_workspace_size) exceeds
+ * GQA_NOALLOC_SCRATCH_BYTES return GQA_ERR_SCRATCH before any HIP call; that covers up
+ * to 128 packed rows per KV group at d_h = 128 (256 at d_h = 64) with the default
+ * workgroup count. Every call on one GPU shares that GPU's array and leaves it holding
+ * its partials: calls that overlap in time on one GPU (two streams, two host threads)
+ * race and must be serialised by the caller. Nothing in the array needs clearing
+ * between calls: each call writes every partial it reads. Errors are those of
+ * gqa_decode, with GQA_ERR_SCRATCH in place of GQA_ERR_WORKSPACE, and GQA_ERR_HIP if
+ * the array's device address cannot be obtained.
+ */
+int gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, const int32_t* block_table, void* out,
+                       int B, int H, int G, int d_h, int q_len, float scale,
+                       void* stream, const gqa_decode_opts* opts);
 
 /* The plan gqa_decode would use for these sizes (validation included). */
 int gqa_decode_plan(int B, int H, int G, int d_h, int q_len,

@@ -335,3 +335,37 @@ def test_latent_paged_geometry_checks():
     assert lcall(bt=P, o=opts(**good)) == WS              # valid; only the workspace is missing
     for bad in (dict(page_size=8), dict(max_blocks_per_seq=0), dict(num_pages=0)):
         assert lcall(bt=P, o=opts(**{**good, **bad})) == INV, bad
+
+
+def call_noalloc(B=2, H=8, G=2, d=128, q_len=1, scale=0.1, o=None, q=P, k=P, v=P, sl=P, bt=None, out=P):
+    o = opts() if o is None else o
+    return _lib.lib().gqa_decode_noalloc(q, k, v, sl, bt, out, B, H, G, d, q_len, ctypes.c_float(scale), None,
+                                         ctypes.byref(o) if o is not False else None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INV), (dict(out=P + 4), INV), (dict(B=0), INV), (dict(H=8, G=3), INV),
+    (dict(scale=float("nan")), INV), (dict(d=96), UNS), (dict(o=False), INV),
+])
+def test_noalloc_rejects_what_gqa_decode_rejects(kw, status):
+    assert call_noalloc(**kw) == status == call(**kw)
+
+
+def test_noalloc_refuses_plans_beyond_its_scratch():
+    """Plans whose partials exceed the fixed scratch return GQA_ERR_SCRATCH before any
+    HIP call; the limit is the one the header states."""
+    SCR = _lib.GQA_ERR_SCRATCH
+    assert _lib.NOALLOC_SCRATCH_BYTES == 65 << 20
+    hdr = open(os.path.join(ROOT, "include", "gqa_decode.h")).read()
+    assert re.search(r"#define GQA_NOALLOC_SCRATCH_BYTES \(\(size_t\)65 << 20\)", hdr)
+    # 256 packed rows per group (G = 1, H = 32, q_len = 8): 512 workgroups x 2 slots x
+    # 256 rows x 128 x 4 bytes = 128 MiB of partials
+    o = opts(cache_capacity=4096)
+    st, pl = plan(B=8, H=32, G=1, q_len=8, o=o)
+    assert st == OK and pl.workspace_bytes > _lib.NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(B=8, H=32, G=1, q_len=8, o=o) == SCR
+    # the same shape at 128 rows needs 64.5 MiB and is not refused on size (it proceeds
+    # to the device, which this host test does not reach: checked on the GPU)
+    st, pl = plan(B=8, H=32, G=1, q_len=4, o=o)
+    assert st == OK and pl.workspace_bytes <= _lib.NOALLOC_SCRATCH_BYTES
+    assert "scratch" in _lib.status_string(SCR)
