@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "GQA decode KV GB/s (% of MI355X HBM peak) and tokens/s at 1 GPU"
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak (no sparsity)
-KERNEL_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "gqa_internal.h")
+KERNEL_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "gqa_internal.h", "mfma_common.h")
 
 
 def kernel_source_hash() -> str:

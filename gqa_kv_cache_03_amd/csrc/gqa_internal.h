@@ -75,6 +75,9 @@ hipError_t launch_merge(const DecodeParams& p, int dtype, int d_h, hipStream_t s
                         hipEvent_t stop);
 hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t stream, hipEvent_t start,
                                    hipEvent_t stop);
+// With a head -> KV head map: NaN into the (token, head) rows of `out` that no packed
+// group tile holds (oversize groups, map entries outside [0, G)); bf16 only.
+hipError_t launch_fill_unmapped(const DecodeParams& p, int d_h, hipStream_t stream);
 // Writes k_new / v_new into the cache rows of the new tokens (vector-ALU path).
 hipError_t launch_append(const DecodeParams& p, int elem_bytes, int d_h, bool paged, hipStream_t stream);
 

@@ -436,7 +436,55 @@ hipError_t go_persistent(const DecodeParams& p, hipStream_t stream, hipEvent_t s
   return hipGetLastError();
 }
 
+// With a call-time head -> KV head map, the packed tile of KV group g holds the rows
+// r = t * n_g + k (token t, k-th head of the group in ascending order) below
+// cap = n_row_blocks * row_block. A group larger than the planned bound leaves its rows
+// r >= cap uncomputed, and a head whose map entry lies outside [0, G) belongs to no
+// group: the decode kernel never writes those (token, head) rows of `out`. This kernel
+// writes NaN into exactly those rows, so that `out` is always fully overwritten and a
+// bad map shows up in the result. One workgroup per (sequence, token).
+__global__ __launch_bounds__(kThreads) void fill_unmapped_rows_kernel(DecodeParams p, int d_h) {
+  __shared__ int grp[kThreads];
+  __shared__ unsigned char dropped[kThreads];
+  const int tid = threadIdx.x;
+  const int bt = blockIdx.x;  // b * q_len + t
+  const int t = bt % p.q_len;
+  if (tid < p.H) grp[tid] = p.head_group[tid];
+  __syncthreads();
+  if (tid < p.H) {
+    const int g = grp[tid];
+    bool drop = g < 0 || g >= p.G;
+    if (!drop) {
+      int k = 0, n_g = 0;
+      for (int h = 0; h < p.H; ++h) {
+        if (grp[h] == g) {
+          k += h < tid;
+          ++n_g;
+        }
+      }
+      drop = t * n_g + k >= p.n_row_blocks * p.row_block;
+    }
+    dropped[tid] = drop ? 1 : 0;
+  }
+  __syncthreads();
+  // the rows to fill, d_h / 4 lanes per head
+  const int lph = d_h / 4;
+  for (int i = tid; i < p.H * lph; i += kThreads) {
+    const int h = i / lph;
+    if (!dropped[h]) continue;
+    const size_t off = ((size_t)bt * p.H + h) * d_h + (i % lph) * 4;
+    put4<__bf16>(static_cast<__bf16*>(p.out) + off, f32x4{__builtin_nanf(""), __builtin_nanf(""),
+                                                          __builtin_nanf(""), __builtin_nanf("")});
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fill_unmapped(const DecodeParams& p, int d_h, hipStream_t stream) {
+  if (p.H > kThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fill_unmapped_rows_kernel, dim3(p.B * p.q_len), dim3(kThreads), 0, stream, p, d_h);
+  return hipGetLastError();
+}
 
 hipError_t launch_merge_persistent(const DecodeParams& p, int d_h, hipStream_t stream, hipEvent_t start,
                                    hipEvent_t stop) {

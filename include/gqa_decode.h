@@ -98,7 +98,11 @@ typedef struct gqa_decode_opts {
    *               need not be 0 then; a KV head may serve any number of query heads.
    *  max_group_heads  with head_group: an upper bound on the query heads of any one
    *               KV head (0: H); it sizes the packed tile. A larger group is an error
-   *               the device cannot report: its surplus heads are left unwritten.
+   *               the host cannot see (the map lives on the device): the (token, head)
+   *               rows that do not fit the packed tile (row t * n_g + k of a group of
+   *               n_g heads, k-th head in ascending order, at or beyond the tile's
+   *               rows) are written as NaN, and so are the rows of any head whose
+   *               entry lies outside [0, G). `out` is always fully overwritten.
    *  head_active  device uint8 [B, q_len, H]: 0 marks a (token, head) pair that a
    *               router left inactive (Grouped Query Experts: k query heads per token
    *               and group); its output row is 0. Every K/V byte is still read: the

@@ -20,4 +20,5 @@ from .gqla_oracle import (  # noqa: F401
     expand_cache,
     gqla_decode,
     latent_bytes,
+    touched_latent_rows,
 )

@@ -12,8 +12,8 @@ Sources (page title, section):
   mask), O = einsum(bhnm, bmv -> bhnv) -- and the decode cache shapes [b, H, m, d_k]
   (MHA) and [b, m, d_k] (MQA).
 * same page, "Grouped-Query Attention" > "Mathematical Formulation": H query heads
-  in G groups of H/G; each group's key and value head is broadcast to the H/G
-  query heads of the group; the cache is [b, G, m, d_k].
+  in G groups of H/G; the group's one key and value head is shared by the group's
+  H/G query heads; the cache is [b, G, m, d_k].
 * "Grouped-Query Attention" (aiwiki), the PyTorch listing: KV head g is expanded
   with repeat_interleave(h // g) -- contiguous blocks of H/G query heads share one
   KV head -- and attention is scaled_dot_product_attention(q, k, v, is_causal),
@@ -37,7 +37,10 @@ Readings where the pages leave a point open (each also listed in the design note
 
 Parity: pinned (see tests/test_oracle.py) by the MHA and MQA reductions, the
 library-routine cross-check with repeat_interleave + SDPA, closed forms (mean of V,
-one-hot), 50-digit brute force on tiny shapes, invariants and the byte count.
+one-hot), 50-digit brute force on tiny shapes, invariants and the byte count. One
+part is parity unpinned: with head_active, an inactive (token, head) pair's output is
+0 -- a reading (no page gives a value for a head the router leaves out), restated by
+its test, not derived from anything the pages fix.
 """
 from __future__ import annotations
 
@@ -53,8 +56,8 @@ def bf16_bits_to_float64(bits: np.ndarray) -> np.ndarray:
 
 def group_of_head(h: int, H: int, G: int) -> int:
     """KV head read by query head h: contiguous blocks of H/G heads per group
-    (repeat_interleave in the aiwiki listing; 'broadcast to the H/G query heads
-    in that group' on the llms.blog page)."""
+    (repeat_interleave in the aiwiki listing; on the llms.blog page each group's
+    single key/value head serves all H/G query heads of that group)."""
     return h // (H // G)
 
 
@@ -108,7 +111,8 @@ def gqa_decode(q, k_cache, v_cache, seq_lens, scale: float, G: int,
     head_group  optional [H] KV head of each query head (non-uniform groups)
     head_active optional [B, q_len, H]; 0 marks a (token, head) pair left inactive by a
              per-token router over each group's query heads (Grouped Query Experts,
-             thelatestinai page), whose output is 0: the pair is not computed
+             thelatestinai page), whose output is 0: the pair is not computed (a
+             reading the pages do not fix: parity unpinned)
     returns  out [B, q_len, H, d] float64 (and, if asked, a dict of weights
              {(b, t, h): w[visible]}).
     """

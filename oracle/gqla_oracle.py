@@ -32,14 +32,31 @@ import numpy as np
 from .gqa_oracle import gqa_decode
 
 
-def latent_rows(latent, b: int, L: int, block_table=None, page_size: int = 0) -> np.ndarray:
+def latent_rows(latent, b: int, L: int, block_table=None, page_size: int = 0,
+                touched: set | None = None) -> np.ndarray:
     """The first L latent vectors of sequence b, as float64 [L, d_c]: latent[b, j]
-    when contiguous, else slot j % page_size of page block_table[b, j // page_size]."""
+    when contiguous, else slot j % page_size of page block_table[b, j // page_size].
+    With `touched`, the storage location of every row read is added to it."""
     if block_table is None:
+        if touched is not None:
+            touched.update(("c", b, j) for j in range(L))
         return np.asarray(latent[b, :L], dtype=np.float64)
     j = np.arange(L)
     pages = np.asarray(block_table[b])[j // page_size]
+    if touched is not None:
+        touched.update(("p", int(pg), int(sl)) for pg, sl in zip(pages, j % page_size))
     return np.asarray(latent[pages, j % page_size], dtype=np.float64)
+
+
+def touched_latent_rows(latent, seq_lens, block_table=None, page_size: int = 0) -> int:
+    """Distinct latent rows (d_c numbers each) that the step reads, counted explicitly
+    from the storage locations of every visible position of every sequence: the
+    independent side of the latent byte-count pin (every group and head derives its
+    keys and values from these same rows)."""
+    seen: set = set()
+    for b in range(len(seq_lens)):
+        latent_rows(latent, b, int(seq_lens[b]), block_table, page_size, seen)
+    return len(seen)
 
 
 def expand_cache(latent, w, seq_lens, block_table=None, page_size: int = 0) -> np.ndarray:

@@ -35,7 +35,7 @@ def test_traffic_figure_follows_the_kernel_sources(monkeypatch):
 
 
 def test_kernel_source_hash_covers_the_decode_sources():
-    assert set(bench.KERNEL_SOURCES) == {"decode_mfma.hip", "decode_valu.hip", "gqa_internal.h"}
+    assert set(bench.KERNEL_SOURCES) == {"decode_mfma.hip", "decode_valu.hip", "gqa_internal.h", "mfma_common.h"}
     h = bench.kernel_source_hash()
     assert len(h) == 16 and int(h, 16) >= 0
     assert h == bench.kernel_source_hash()

@@ -139,3 +139,42 @@ def test_variants_reject_unsupported():
     hg = torch.zeros(8, dtype=torch.int32, device="cuda")
     with pytest.raises(GqaError):            # fp32: the variants run on the matrix cores only
         gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, head_group=hg)
+
+
+@pytest.mark.parametrize("splits", [0, 5])
+def test_oversize_group_and_stray_entries_give_nan_rows(splits):
+    """A map whose group exceeds max_group_heads, and entries outside [0, G): the
+    (token, head) rows no packed tile holds come back NaN, every other row matches
+    the oracle, and nothing is left unwritten (out starts out as a finite canary)."""
+    from gqa_kv_cache_03_amd import gqa_decode, plan
+    B, H, G, d, q_len, maxh = 2, 32, 4, 128, 2, 6
+    wl, lens = small_workload(B, H, G, d, q_len, [300, 900], seed=3700)
+    inp = make(wl, lens)
+    rng = np.random.default_rng(3710)
+    m = rng.permutation(np.concatenate([np.zeros(10), np.repeat([1, 2, 3], 6), [-1, 7],
+                                        rng.integers(1, 4, H - 30)])).astype(np.int32)
+    pl = plan(inp.q, inp.k_cache, causal=True, head_group=torch.as_tensor(m, device="cuda"),
+              max_group_heads=maxh)
+    assert pl["row_blocks"] == 1 and pl["rows"] == maxh * q_len
+    cap = maxh * q_len
+    drop = np.zeros((q_len, H), dtype=bool)
+    for h in range(H):
+        g = int(m[h])
+        if not 0 <= g < G:
+            drop[:, h] = True
+            continue
+        members = [x for x in range(H) if m[x] == g]
+        k = members.index(h)
+        for t in range(q_len):
+            drop[t, h] = t * len(members) + k >= cap
+    assert drop.any() and (~drop).any()
+    out = torch.full_like(inp.q, 7.0)
+    gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, scale=wl.scale, out=out, num_splits=splits,
+               head_group=torch.as_tensor(m, device="cuda"), max_group_heads=maxh)
+    torch.cuda.synchronize()
+    got = host64(out)
+    safe = np.where((m >= 0) & (m < G), m, 0).astype(np.int32)
+    ref = oracle_variant(inp, head_group=safe)
+    for b in range(B):
+        assert np.isnan(got[b][drop]).all()
+        assert_parity(got[b][~drop], ref[b][~drop], "bfloat16", f"kept rows b={b}")

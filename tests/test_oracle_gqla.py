@@ -162,12 +162,27 @@ def test_paged_latent_equals_contiguous_exactly(P):
     assert np.array_equal(ref, got)
 
 
-def test_latent_bytes_count_each_token_once():
-    lens = [1000, 37, 4096]
-    assert oracle.latent_bytes(512, 2, lens) == 512 * 2 * sum(lens)
-    # against the expanded cache of the same layer: 2 G d_h / d_c times the bytes
-    G, d_h = 16, 128
-    assert oracle.kv_bytes(G, d_h, 2, lens) == oracle.latent_bytes(512, 2, lens) * 2 * G * d_h // 512
+@pytest.mark.parametrize("P", [0, 3, 4])
+def test_latent_bytes_count_each_token_once(P):
+    """latent_bytes against an explicit count of the distinct latent rows (storage
+    locations) the step reads, contiguous and paged with a permuted table: every
+    visible token's latent is read once, whatever the number of heads and groups."""
+    rng = np.random.default_rng(760 + P)
+    lens = [9, 2, 14, 5]
+    d_c = 6
+    lat = rng.standard_normal((len(lens), max(lens) + 3, d_c))
+    if P:
+        pool, tbl = paginate_latent(np.random.default_rng(P), lat, np.asarray(lens), P)
+        rows = oracle.touched_latent_rows(pool, lens, tbl, P)
+    else:
+        rows = oracle.touched_latent_rows(lat, lens)
+    assert rows == sum(lens)
+    assert oracle.latent_bytes(d_c, 2, lens) == d_c * 2 * rows
+    # the expanded cache of the same layer reads 2 G d_h numbers per token instead of d_c
+    G, d_h = 3, 4
+    k = np.zeros((len(lens), G, max(lens), d_h))
+    assert oracle.kv_bytes(G, d_h, 2, lens) == oracle.touched_kv_rows(k, k, lens, G) * d_h * 2
+    assert oracle.kv_bytes(G, d_h, 2, lens) * d_c == oracle.latent_bytes(d_c, 2, lens) * 2 * G * d_h
 
 
 # --------------------------------------------------------------- planted mistakes
