@@ -74,6 +74,8 @@ CASES = [
     (2, 4, 2, 128, 1, [5, 70], 0),             # 4 rows
     (2, 16, 2, 128, 1, [1, 2], 0),             # a single visible token
     (2, 16, 2, 128, 4, [4, 37], 16),           # L = q_len: the first new token sees one key
+    (1, 64, 2, 128, 1, [300], 0),              # 32 heads per group: two 16-row projection rounds
+    (2, 48, 1, 64, 2, [50, 333], 16),          # 48 heads in one group, d_h 64: three rounds
 ]
 
 
