@@ -406,21 +406,36 @@ def roofline_of(m, traffic_key):
     }
 
 
-def per_config_entry(m):
-    """One long-context configuration's line in the default run."""
-    value = m["kv_bytes"] / (m["ms"] * 1e-3) / 1e9
-    r = roofline_of(m, m["wl"].name)
+def per_config_entry(line: dict) -> dict:
+    """One long-context configuration's entry in the default run, from the JSON line that
+    `bench.py --workload NAME` printed for it."""
+    r = line["roofline"]
     return {
-        "step_us": round(m["ms"] * 1e3, 2),
-        "kv_gbps": round(value, 1),
-        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "tokens_per_s": round(m["wl"].B * m["wl"].q_len / (m["ms"] * 1e-3), 1),
-        "decode_us": round(m["dec_ms"] * 1e3, 2),
-        "merge_us": round(m["mrg_ms"] * 1e3, 2),
+        "step_us": round(line["ms_per_step"] * 1e3, 2),
+        "kv_gbps": round(line["value"], 1),
+        "pct_of_hbm_peak": line["pct_of_hbm_peak"],
+        "tokens_per_s": line["tokens_per_s"],
+        "decode_us": round(line["kernel_ms"]["split_decode"] * 1e3, 2),
+        "merge_us": round(line["kernel_ms"]["lse_merge"] * 1e3, 2),
         "decode_roofline_frac": r["frac"],
         "roofline_bound": r["bound"],
         "traffic": r["traffic"],
     }
+
+
+def measure_in_child(name: str, warmup: int, steps: int) -> dict:
+    """`bench.py --workload NAME` in a process of its own (the parent waits for it), so that
+    every configuration starts from a fresh device context and allocator, as a
+    stand-alone run of it does; returns the child's JSON line."""
+    import subprocess
+    cmd = [sys.executable, os.path.abspath(__file__), "--workload", name, "--warmup", str(warmup),
+           "--steps", str(steps), "--no-cpu-baseline", "--no-ceiling"]
+    print(f"[bench] per-config: {name}", file=sys.stderr, flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=sys.stderr, text=True, timeout=600)
+    if r.returncode != 0:
+        raise RuntimeError(f"per-config run of {name} failed with status {r.returncode}")
+    lines = [x for x in r.stdout.strip().splitlines() if x.startswith("{")]
+    return json.loads(lines[-1])
 
 
 def main():
@@ -490,18 +505,14 @@ def main():
     torch.cuda.empty_cache()
     if args.workload is None and not args.no_per_config:
         # the default run also measures every other long-context configuration with plain
-        # calls (no append or grouping variant)
+        # calls (no append or grouping variant), each in a child process of its own
         # (at least 50 warm-up and 100 timed steps each, so that short runs still report
         # settled clocks for these shorter steps)
         res["per_config"] = {}
-        pc_args = argparse.Namespace(**vars(args))
-        pc_args.warmup, pc_args.steps = max(args.warmup, 50), max(args.steps, 100)
-        res["per_config_protocol"] = {"warmup": pc_args.warmup, "steps": pc_args.steps}
+        warm, steps = max(args.warmup, 50), max(args.steps, 100)
+        res["per_config_protocol"] = {"warmup": warm, "steps": steps, "process": "one child process per configuration"}
         for other in BENCH_PER_CONFIG:
-            mo = measure(other, pc_args, dev, variant_opts=False)
-            res["per_config"][other] = per_config_entry(mo)
-            del mo
-            torch.cuda.empty_cache()
+            res["per_config"][other] = per_config_entry(measure_in_child(other, warm, steps))
     print(json.dumps(res), flush=True)
 
 

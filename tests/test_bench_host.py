@@ -39,3 +39,14 @@ def test_kernel_source_hash_covers_the_decode_sources():
     h = bench.kernel_source_hash()
     assert len(h) == 16 and int(h, 16) >= 0
     assert h == bench.kernel_source_hash()
+
+
+def test_per_config_entry_reads_a_child_line():
+    import bench
+    line = {"ms_per_step": 0.1105, "value": 4860.0, "pct_of_hbm_peak": 60.75, "tokens_per_s": 289592.8,
+            "kernel_ms": {"split_decode": 0.1012, "lse_merge": 0.0083},
+            "roofline": {"frac": 0.6633, "bound": "hbm", "traffic": None}}
+    e = bench.per_config_entry(line)
+    assert e == {"step_us": 110.5, "kv_gbps": 4860.0, "pct_of_hbm_peak": 60.75, "tokens_per_s": 289592.8,
+                 "decode_us": 101.2, "merge_us": 8.3, "decode_roofline_frac": 0.6633, "roofline_bound": "hbm",
+                 "traffic": None}
