@@ -33,6 +33,7 @@ EXPORTED = (
     "gqa_decode",
     "gqa_decode_append",
     "gqa_decode_noalloc",
+    "gqa_decode_check_inputs",
     "gqa_decode_plan",
     "gqa_decode_workspace_size",
     "gqa_status_string",
@@ -127,6 +128,8 @@ def lib() -> ctypes.CDLL:
     L.gqa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_float,
                                     vp, ctypes.POINTER(DecodeOpts)]
     L.gqa_decode_append.restype = i32
+    L.gqa_decode_check_inputs.argtypes = [vp, vp, i32, i32, vp, ctypes.POINTER(DecodeOpts), vp]
+    L.gqa_decode_check_inputs.restype = i32
     L.gqa_decode_plan.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(DecodeOpts), ctypes.POINTER(Plan)]
     L.gqa_decode_plan.restype = i32
     L.gqa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(DecodeOpts),

@@ -516,6 +516,36 @@ int gqa_decode_append(const void* q, const void* k_new, const void* v_new, void*
                      scale, stream, opts);
 }
 
+int gqa_decode_check_inputs(const int32_t* seq_lens, const int32_t* block_table, int B, int q_len, void* stream,
+                            const gqa_decode_opts* opts, int32_t* report) {
+  if (!seq_lens || !report || !opts || opts->struct_size < sizeof(gqa_decode_opts)) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned(seq_lens, 4) || !aligned(report, 4) || (block_table && !aligned(block_table, 4)))
+    return GQA_ERR_INVALID_ARGUMENT;
+  if (B <= 0 || q_len <= 0) return GQA_ERR_INVALID_ARGUMENT;
+  gqa::CheckParams cp{};
+  cp.seq_lens = seq_lens;
+  cp.table = block_table;
+  cp.report = report;
+  cp.B = B;
+  cp.q_len = q_len;
+  if (block_table) {
+    const int P = opts->page_size;
+    if (P < 16 || P > 256 || (P & (P - 1)) != 0) return GQA_ERR_INVALID_ARGUMENT;
+    if (opts->max_blocks_per_seq <= 0 || opts->num_pages <= 0) return GQA_ERR_INVALID_ARGUMENT;
+    if ((long long)opts->max_blocks_per_seq * P > INT32_MAX / 2) return GQA_ERR_UNSUPPORTED;
+    if ((long long)B * opts->max_blocks_per_seq > INT32_MAX) return GQA_ERR_UNSUPPORTED;
+    cp.page_size = P;
+    cp.max_blocks = opts->max_blocks_per_seq;
+    cp.num_pages = opts->num_pages;
+    cp.capacity = opts->max_blocks_per_seq * P;
+  } else {
+    if (opts->page_size != 0 || opts->cache_capacity <= 0) return GQA_ERR_INVALID_ARGUMENT;
+    cp.capacity = opts->cache_capacity;
+  }
+  if (gqa::launch_check_inputs(cp, static_cast<hipStream_t>(stream)) != hipSuccess) return GQA_ERR_HIP;
+  return GQA_OK;
+}
+
 int gqla_absorb_plan(int B, int H, int G, int d_h, int d_c, int q_len, const gqa_decode_opts* opts,
                      gqa_plan* plan) {
   if (!plan || !opts) return GQA_ERR_INVALID_ARGUMENT;

@@ -91,6 +91,15 @@ struct LatentProjParams {
 };
 hipError_t launch_latent_absorb_q(const LatentProjParams& p, hipStream_t stream);
 
+// Device-side check of the decode calls' device-resident preconditions (check.hip).
+struct CheckParams {
+  const int32_t* seq_lens;  // [B]
+  const int32_t* table;     // [B, max_blocks] or nullptr
+  int32_t* report;          // [4]: bad lengths, bad entries, first bad sequence, first bad entry
+  int B, q_len, capacity, page_size, max_blocks, num_pages;
+};
+hipError_t launch_check_inputs(const CheckParams& p, hipStream_t stream);
+
 // Geometry of the MFMA kernel variants, chosen by packed row count R.
 struct MfmaVariant {
   int max_rows;      // R this variant serves (multiple of 16)

@@ -74,6 +74,30 @@ def plan(q, k_cache, block_table=None, *, causal=True, num_splits=0, chunk_token
     return pl.as_dict()
 
 
+def check_inputs(seq_lens, block_table=None, *, q_len: int, capacity: int = 0, page_size: int = 0,
+                 num_pages: int = 0) -> dict:
+    """Device-side check of a decode call's device-resident preconditions
+    (gqa_decode_check_inputs): every length in [q_len, capacity] and every block-table
+    entry the step reads in [0, num_pages). Contiguous caches give `capacity`; paged ones
+    `page_size` and `num_pages` (the table gives max_blocks_per_seq). Waits for the result
+    on the current stream and returns the counts and the first offenders (None if none)."""
+    import torch
+    B = seq_lens.shape[0]
+    o = make_opts(dtype_code=_lib.GQA_DTYPE_BF16, causal=True, capacity=capacity if block_table is None else 0,
+                  page_size=page_size if block_table is not None else 0,
+                  max_blocks=block_table.shape[1] if block_table is not None else 0, num_pages=num_pages)
+    report = torch.empty(4, dtype=torch.int32, device=seq_lens.device)
+    st = _lib.lib().gqa_decode_check_inputs(
+        seq_lens.data_ptr(), None if block_table is None else block_table.data_ptr(), B, q_len,
+        torch.cuda.current_stream(seq_lens.device).cuda_stream, ctypes.byref(o), report.data_ptr())
+    if st != _lib.GQA_OK:
+        raise GqaError(st, "gqa_decode_check_inputs")
+    r = [int(x) for x in report.cpu()]
+    none = 2 ** 31 - 1
+    return {"bad_lengths": r[0], "bad_entries": r[1], "first_bad_sequence": None if r[2] == none else r[2],
+            "first_bad_entry": None if r[3] == none else r[3]}
+
+
 def gqa_decode(q, k_cache, v_cache, seq_lens, block_table=None, *, scale: Optional[float] = None,
                out=None, causal: bool = True, num_splits: int = 0, chunk_tokens: int = 0,
                policy: str = "auto", workspace=None, profile_events=None, head_group=None,

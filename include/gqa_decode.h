@@ -225,6 +225,32 @@ int gqa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
                        int B, int H, int G, int d_h, int q_len, float scale,
                        void* stream, const gqa_decode_opts* opts);
 
+/*
+ * gqa_decode_check_inputs -- checks on the device the preconditions that gqa_decode,
+ * gqa_decode_noalloc, gqa_decode_append and gqla_absorb_decode document for data in
+ * device memory but do not verify: q_len <= seq_lens[b] <= capacity for every b, and,
+ * with a block table, every entry a step reads (entry k of row b for
+ * k < ceil(seq_lens[b] / page_size)) in [0, num_pages). A paged cache is reached
+ * through that table ("PagedAttention", llms.blog GQA/MQA page), so a stray entry is
+ * the caller mistake that would make a decode kernel read memory it does not own. For
+ * debugging: call it with the seq_lens, block_table, B, q_len and opts of a decode call
+ * (capacity or page geometry are read from opts, as there).
+ *
+ *   report  device int32[4], 4-byte aligned, written by the call: [0] sequences with a
+ *           bad length, [1] bad table entries among those read (a row whose length is
+ *           bad is checked up to the length clamped to [1, capacity], as the kernels
+ *           clamp it), [2] the first bad sequence, [3] the first bad entry as
+ *           b * max_blocks_per_seq + k; INT32_MAX in [2] and [3] when there is none.
+ *
+ * Asynchronous on `stream`; read report after synchronising. Allocates nothing and
+ * clears report itself (a kernel, not a memset, so it can be captured in a graph).
+ * Errors: INVALID_ARGUMENT for NULL or misaligned seq_lens / block_table / report,
+ * B <= 0, q_len <= 0, a bad opts struct or paged geometry (as gqa_decode);
+ * UNSUPPORTED when B * max_blocks_per_seq exceeds INT32_MAX; HIP when a launch fails.
+ */
+int gqa_decode_check_inputs(const int32_t* seq_lens, const int32_t* block_table, int B, int q_len,
+                            void* stream, const gqa_decode_opts* opts, int32_t* report);
+
 /* The plan gqa_decode would use for these sizes (validation included). */
 int gqa_decode_plan(int B, int H, int G, int d_h, int q_len,
                     const gqa_decode_opts* opts, gqa_plan* plan);

@@ -369,3 +369,31 @@ def test_noalloc_refuses_plans_beyond_its_scratch():
     st, pl = plan(B=8, H=32, G=1, q_len=4, o=o)
     assert st == OK and pl.workspace_bytes <= _lib.NOALLOC_SCRATCH_BYTES
     assert "scratch" in _lib.status_string(SCR)
+
+
+def ccall(sl=P, bt=None, B=2, q_len=1, o=None, report=P):
+    o = opts() if o is None else o
+    return _lib.lib().gqa_decode_check_inputs(sl, bt, B, q_len, None, ctypes.byref(o) if o is not False else None,
+                                              report)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sl=None), INV), (dict(report=None), INV), (dict(o=False), INV),
+    (dict(sl=P + 2), INV), (dict(report=P + 2), INV), (dict(bt=P + 2, o="paged"), INV),
+    (dict(B=0), INV), (dict(q_len=0), INV),
+    (dict(o=dict(page_size=16)), INV),                          # page size without a table
+    (dict(o=dict(cache_capacity=0)), INV),
+    (dict(bt=P, o=dict(page_size=24, max_blocks_per_seq=4, num_pages=8)), INV),
+    (dict(bt=P, o=dict(page_size=16, max_blocks_per_seq=0, num_pages=8)), INV),
+    (dict(bt=P, o=dict(page_size=16, max_blocks_per_seq=4, num_pages=0)), INV),
+    (dict(bt=P, B=65536, o=dict(page_size=16, max_blocks_per_seq=40000, num_pages=8)), UNS),
+])
+def test_check_inputs_rejects_bad_arguments(kw, status):
+    """Argument errors of gqa_decode_check_inputs come back before any HIP call."""
+    kw = dict(kw)
+    o = kw.pop("o", None)
+    if o == "paged":
+        o = opts(page_size=16, max_blocks_per_seq=4, num_pages=8)
+    elif isinstance(o, dict):
+        o = opts(**o)
+    assert ccall(o=o, **kw) == status
