@@ -19,6 +19,7 @@ from .gqla_oracle import (  # noqa: F401
     latent_rows,
     expand_cache,
     gqla_decode,
+    append_latent,
     latent_bytes,
     touched_latent_rows,
 )

@@ -95,6 +95,31 @@ def gqla_decode(q, latent, w_uk, w_uv, seq_lens, scale: float, block_table=None,
     return gqa_decode(q, k, v, seq_lens, scale, G, causal=causal)
 
 
+def append_latent(latent, new, seq_lens, block_table=None, page_size: int = 0) -> np.ndarray:
+    """The latent cache after a step's new tokens are added to it, as a float64 copy.
+
+    Every cached token keeps one joint latent vector (the GQLA abstract), so a decode
+    step adds one row per new token. Reading (the same as for the plain GQA cache): the
+    step's q_len new tokens are the last q_len of the seq_lens[b] positions, so row t of
+    new[b] (new is [B, q_len, d_c]) becomes position seq_lens[b] - q_len + t of
+    sequence b -- latent[b, pos] when contiguous, or slot pos % page_size of page
+    block_table[b, pos // page_size] when paged. No other row changes.
+    """
+    out = np.array(latent, dtype=np.float64, copy=True)
+    new = np.asarray(new, dtype=np.float64)
+    B, q_len, _ = new.shape
+    for b in range(B):
+        L = int(seq_lens[b])
+        assert q_len <= L, "every new token must be in the cache"
+        for t in range(q_len):
+            pos = L - q_len + t
+            if block_table is None:
+                out[b, pos] = new[b, t]
+            else:
+                out[int(block_table[b, pos // page_size]), pos % page_size] = new[b, t]
+    return out
+
+
 def latent_bytes(d_c: int, itemsize: int, seq_lens) -> int:
     """Latent-cache bytes one absorbed decode step must read: each visible token's
     latent once, d_c * itemsize * sum_b L_b (the expanded cache would need

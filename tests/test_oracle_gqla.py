@@ -225,3 +225,64 @@ def test_planted_page_slot_mistake_is_caught(monkeypatch):
     pool, tbl = paginate_latent(np.random.default_rng(3), lat, lens, 3, extra=0)
     ref = GL.gqla_decode(q, pool, w_uk, w_uv, lens, 0.6, block_table=tbl, page_size=3)
     assert not np.allclose(ref, absorbed(q, lat, w_uk, w_uv, lens, 0.6), rtol=0, atol=1e-6)
+
+
+# ------------------------------ the latent append (oracle.append_latent)
+
+def _latent_append_case(rng, q_len=3):
+    old_lens = np.array([5, 1, 9], dtype=np.int32)
+    lens = old_lens + q_len
+    cap = int(lens.max()) + 2
+    B, d_c = len(lens), 6
+    old = np.full((B, cap, d_c), np.nan)
+    for b in range(B):
+        old[b, :old_lens[b]] = rng.standard_normal((old_lens[b], d_c))
+    new = rng.standard_normal((B, q_len, d_c))
+    return old, new, old_lens, lens
+
+
+def test_latent_append_places_new_rows_after_the_old_ones():
+    old, new, old_lens, lens = _latent_append_case(np.random.default_rng(91))
+    got = oracle.append_latent(old, new, lens)
+    for b in range(len(lens)):
+        exp = np.concatenate([old[b, :old_lens[b]], new[b]], axis=0)     # the sequence grows by q_len rows
+        np.testing.assert_array_equal(got[b, :lens[b]], exp)
+        assert np.isnan(got[b, lens[b]:]).all()                           # nothing past the sequence
+    assert np.isnan(old[1, old_lens[1]:]).all()                           # the input is not modified
+
+
+def test_latent_append_then_expand_equals_expand_then_gqa_append():
+    """Appending a latent row and expanding it through the group's projections gives the
+    row the plain GQA append writes for that group (W c_new): the two oracle appends agree
+    through expand_cache."""
+    rng = np.random.default_rng(92)
+    old, new, old_lens, lens = _latent_append_case(rng, q_len=2)
+    G, d_h = 2, 3
+    w = rng.standard_normal((G, d_h, old.shape[2]))
+    via_latent = GL.expand_cache(oracle.append_latent(old, new, lens), w, lens)
+    new_kv = np.einsum("gic,btc->btgi", w, new)                             # [B, q_len, G, d_h]
+    via_kv = oracle.append_kv(GL.expand_cache(old, w, lens), new_kv, lens)
+    for b in range(len(lens)):
+        np.testing.assert_allclose(via_latent[b, :, :lens[b]], via_kv[b, :, :lens[b]], rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("P", [2, 4])
+def test_latent_append_paged_equals_contiguous(P):
+    old, new, old_lens, lens = _latent_append_case(np.random.default_rng(93))
+    zero = np.nan_to_num(old, nan=0.0)
+    pool, tbl = paginate_latent(np.random.default_rng(P), zero, lens, P)
+    pool_after = oracle.append_latent(pool, new, lens, block_table=tbl, page_size=P)
+    contig_after = oracle.append_latent(zero, new, lens)
+    for b in range(len(lens)):
+        for j in range(lens[b]):
+            np.testing.assert_array_equal(pool_after[tbl[b, j // P], j % P], contig_after[b, j])
+
+
+def test_planted_latent_append_position_mistake_is_caught():
+    old, new, old_lens, lens = _latent_append_case(np.random.default_rng(94))
+    wrong = np.array(old, copy=True)
+    for b in range(len(lens)):                  # off by one: the new rows one slot late
+        for t in range(new.shape[1]):
+            wrong[b, lens[b] - new.shape[1] + t + 1] = new[b, t]
+    assert not all(np.array_equal(wrong[b, :lens[b]], np.concatenate([old[b, :old_lens[b]], new[b]]))
+                   for b in range(len(lens)))
