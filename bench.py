@@ -9,7 +9,8 @@ also carries `per_config`: the same measurement on the other long-context
 configurations (ragged, paged, and the group sweep at G = 1, 2, 4, 8).
 
 A step is one gqa_decode call (gqa_decode_append with --append; gqla_absorb_decode for
-a GQLA workload) over the whole batch of the workload, inputs resident in HBM. Several
+a GQLA workload, gqla_absorb_decode_append with --append) over the whole batch of the
+workload, inputs resident in HBM. Several
 copies of the cache are rotated so that every step reads cold data (the 256 MiB
 Infinity Cache cannot serve a step from the previous one). Prints one JSON line:
 
@@ -76,7 +77,8 @@ def parse():
     ap.add_argument("--active-frac", type=float, default=0.0,
                     help="per-(token, head) active mask with this fraction of pairs active (0: no mask)")
     ap.add_argument("--append", action="store_true",
-                    help="time gqa_decode_append: the step also writes the new tokens' K/V into the cache")
+                    help="time the fused append: the step also writes the new tokens' K/V (or latents) "
+                         "into the cache")
     ap.add_argument("--copies", type=int, default=0, help="KV cache copies rotated (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -224,7 +226,8 @@ def measure(name, args, dev, variant_opts=True, ceiling=False):
     import numpy as np
     import torch
 
-    from gqa_kv_cache_03_amd import gqa_decode, gqa_decode_append, gqla_absorb_decode, gqla_plan, plan, read_stream
+    from gqa_kv_cache_03_amd import (gqa_decode, gqa_decode_append, gqla_absorb_decode, gqla_absorb_decode_append,
+                                     gqla_plan, plan, read_stream)
     from gqa_synth import make_inputs, make_latent_inputs, workload
 
     wl = workload(name)
@@ -232,8 +235,8 @@ def measure(name, args, dev, variant_opts=True, ceiling=False):
     use_append = args.append and variant_opts
     head_map = args.head_map and variant_opts
     active_frac = args.active_frac if variant_opts else 0.0
-    if latent and (use_append or head_map or active_frac > 0 or args.policy == "valu"):
-        sys.exit("the GQLA absorbed path takes no --append, --head-map, --active-frac or valu policy")
+    if latent and (head_map or active_frac > 0 or args.policy == "valu"):
+        sys.exit("the GQLA absorbed path takes no --head-map, --active-frac or valu policy")
     print(f"[bench] generating {name}", file=sys.stderr, flush=True)
     if latent:
         inp = make_latent_inputs(wl, device=dev)
@@ -278,7 +281,18 @@ def measure(name, args, dev, variant_opts=True, ceiling=False):
     ws = torch.empty(max(pl["workspace_bytes"], 256), dtype=torch.uint8, device=dev)
 
     new_bytes = 0
-    if use_append:
+    if use_append and latent:
+        # the new tokens' latents, as the down-projection would hand them over: [B, q_len, d_c]
+        c_new = torch.empty((wl.B, wl.q_len, wl.d_c), dtype=inp.q.dtype, device=dev)
+        for b in range(wl.B):
+            for t in range(wl.q_len):
+                pos = int(inp.lens[b]) - wl.q_len + t
+                if inp.block_table is None:
+                    c_new[b, t] = inp.latent[b, pos]
+                else:
+                    c_new[b, t] = inp.latent[int(inp.table[b, pos // wl.page_size]), pos % wl.page_size]
+        new_bytes = c_new.numel() * c_new.element_size()
+    elif use_append:
         # the new tokens' rows, as the projections would hand them over: [B, q_len, G, d_h]
         k_new = torch.empty((wl.B, wl.q_len, wl.G, wl.d_h), dtype=inp.q.dtype, device=dev)
         v_new = torch.empty_like(k_new)
@@ -293,7 +307,10 @@ def measure(name, args, dev, variant_opts=True, ceiling=False):
         new_bytes = 2 * k_new.numel() * k_new.element_size()
 
     def step(i, events=None):
-        if latent:
+        if latent and use_append:
+            gqla_absorb_decode_append(inp.q, c_new, ks[i % copies], inp.w_uk, inp.w_uv, inp.seq_lens,
+                                      inp.block_table, out=out, workspace=ws, profile_events=events, **kw)
+        elif latent:
             gqla_absorb_decode(inp.q, ks[i % copies], inp.w_uk, inp.w_uv, inp.seq_lens, inp.block_table,
                                out=out, workspace=ws, profile_events=events, **kw)
         elif use_append:

@@ -8,5 +8,5 @@
     out = gqla_absorb_decode(q, latent, w_uk, w_uv, seq_lens)  # GQLA, absorbed form
 """
 from .ops import gqa_decode, gqa_decode_append, gqa_decode_noalloc, plan, workspace_bytes, read_stream  # noqa: F401
-from .ops import gqla_absorb_decode, gqla_plan, check_inputs  # noqa: F401
+from .ops import gqla_absorb_decode, gqla_absorb_decode_append, gqla_plan, check_inputs  # noqa: F401
 from ._lib import GqaError, LIB_PATH  # noqa: F401

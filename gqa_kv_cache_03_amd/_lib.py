@@ -41,6 +41,7 @@ EXPORTED = (
     "gqa_bench_read_stream",
     "gqa_bench_read_stream_lds",
     "gqla_absorb_decode",
+    "gqla_absorb_decode_append",
     "gqla_absorb_plan",
     "gqla_absorb_workspace_size",
 )
@@ -146,6 +147,9 @@ def lib() -> ctypes.CDLL:
     L.gqla_absorb_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, ctypes.c_float,
                                      vp, ctypes.POINTER(DecodeOpts)]
     L.gqla_absorb_decode.restype = i32
+    L.gqla_absorb_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                            ctypes.c_float, vp, ctypes.POINTER(DecodeOpts)]
+    L.gqla_absorb_decode_append.restype = i32
     L.gqla_absorb_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(DecodeOpts), ctypes.POINTER(Plan)]
     L.gqla_absorb_plan.restype = i32
     L.gqla_absorb_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(DecodeOpts),

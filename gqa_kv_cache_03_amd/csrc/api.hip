@@ -380,10 +380,12 @@ int make_latent_plan(int B, int H, int G, int d_h, int d_c, int q_len, const gqa
   return GQA_OK;
 }
 
-int latent_impl(const void* q, const void* latent, const void* w_uk, const void* w_uv, const int32_t* seq_lens,
-                const int32_t* block_table, void* out, int B, int H, int G, int d_h, int d_c, int q_len,
-                float scale, void* stream, const gqa_decode_opts* opts) {
+// c_new: the append's new latents [B, q_len, d_c] (nullptr: no append).
+int latent_impl(const void* q, const void* c_new, const void* latent, const void* w_uk, const void* w_uv,
+                const int32_t* seq_lens, const int32_t* block_table, void* out, int B, int H, int G, int d_h,
+                int d_c, int q_len, float scale, void* stream, const gqa_decode_opts* opts) {
   if (!q || !latent || !w_uk || !w_uv || !seq_lens || !out || !opts) return GQA_ERR_INVALID_ARGUMENT;
+  if (c_new && !aligned(c_new, 16)) return GQA_ERR_INVALID_ARGUMENT;
   if (!aligned(q, 16) || !aligned(latent, 16) || !aligned(w_uk, 16) || !aligned(w_uv, 16) ||
       !aligned(out, 16) || !aligned(seq_lens, 4) || (block_table && !aligned(block_table, 4)))
     return GQA_ERR_INVALID_ARGUMENT;
@@ -420,6 +422,10 @@ int latent_impl(const void* q, const void* latent, const void* w_uk, const void*
   dp.q = pp.q_lat;
   dp.k = latent;
   dp.v = latent;
+  // the append: the new tokens' latents are read from c_new and written to the cache by
+  // the kernel that attends over them (the latent is one tensor, so both pointers)
+  dp.k_new = c_new;
+  dp.v_new = c_new;
   dp.seq_lens = seq_lens;
   dp.table = block_table;
   dp.out = ws + lp.q_lat_bytes;
@@ -573,8 +579,17 @@ int gqla_absorb_workspace_size(int B, int H, int G, int d_h, int d_c, int q_len,
 int gqla_absorb_decode(const void* q, const void* latent_cache, const void* w_uk, const void* w_uv,
                        const int32_t* seq_lens, const int32_t* block_table, void* out, int B, int H, int G,
                        int d_h, int d_c, int q_len, float scale, void* stream, const gqa_decode_opts* opts) {
-  return latent_impl(q, latent_cache, w_uk, w_uv, seq_lens, block_table, out, B, H, G, d_h, d_c, q_len, scale,
-                     stream, opts);
+  return latent_impl(q, nullptr, latent_cache, w_uk, w_uv, seq_lens, block_table, out, B, H, G, d_h, d_c, q_len,
+                     scale, stream, opts);
+}
+
+int gqla_absorb_decode_append(const void* q, const void* c_new, const void* w_uk, const void* w_uv,
+                              void* latent_cache, const int32_t* seq_lens, const int32_t* block_table, void* out,
+                              int B, int H, int G, int d_h, int d_c, int q_len, float scale, void* stream,
+                              const gqa_decode_opts* opts) {
+  if (!c_new) return GQA_ERR_INVALID_ARGUMENT;
+  return latent_impl(q, c_new, latent_cache, w_uk, w_uv, seq_lens, block_table, out, B, H, G, d_h, d_c, q_len,
+                     scale, stream, opts);
 }
 
 }  // extern "C"

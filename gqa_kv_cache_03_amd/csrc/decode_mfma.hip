@@ -29,7 +29,8 @@
 // Options handled here as well: the cache append (the new tokens' rows come from
 // k_new / v_new and are copied into the cache from LDS), a call-time head -> KV head
 // map (non-uniform groups) and a per-(token, head) active mask. D = 512 is the GQLA
-// latent of the absorbed execution: one KV head that is both K and V, staged once.
+// latent of the absorbed execution: one KV head that is both K and V, staged once (its
+// append reads the new latents from k_new and writes the one cache).
 //
 // Matrix-core mapping (v_mfma_f32_16x16x32_bf16, A 16x32 / B 32x16 / C 16x16):
 //   S^T = K Q^T with K as the A operand (rows = keys) and Q^T as B (columns = query
@@ -272,14 +273,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   // tile's wait, while nothing else is in flight.
   auto copy_new_rows = [&](const Cursor& c, int f) {
     // every row block of a group stages the same tile; the first one writes it (the
-    // latent path has no append: the host never passes new rows with it)
-    if constexpr (C::SHARED) return;
+    // latent is one tensor: its new rows go to the one cache)
     if (!tile_has_new(c) || c.rb != 0) return;
     const unsigned char* st = smem + (f % NS) * C::STAGE_BYTES;
     const int t0 = c.t * T;
     const int new0 = c.L - p.q_len;
     unsigned char* kc = static_cast<unsigned char*>(const_cast<void*>(p.k));
-    unsigned char* vc = static_cast<unsigned char*>(const_cast<void*>(p.v));
+    [[maybe_unused]] unsigned char* vc = static_cast<unsigned char*>(const_cast<void*>(p.v));
     int pg[T / 16] = {};
     tile_pages(c, pg);
 #pragma unroll
@@ -290,10 +290,12 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
       if (j >= new0 && j < c.L) {  // a new token's row (not a re-read past the end)
         const int slot = n * kThreads * 16 + wave * 1024 + lane * 16;
         const u32x4 kv = *reinterpret_cast<const u32x4*>(st + slot);
-        const u32x4 vv = *reinterpret_cast<const u32x4*>(st + C::TENSOR_BYTES + slot);
         const size_t rb = cache_row(c, pg, row, j);
         *reinterpret_cast<u32x4*>(kc + rb + ((pch ^ swz_k<CPR, C::SHARED>(row)) << 4)) = kv;
-        *reinterpret_cast<u32x4*>(vc + rb + ((pch ^ swz_v<CPR, C::SHARED>(row)) << 4)) = vv;
+        if constexpr (!C::SHARED) {
+          const u32x4 vv = *reinterpret_cast<const u32x4*>(st + C::TENSOR_BYTES + slot);
+          *reinterpret_cast<u32x4*>(vc + rb + ((pch ^ swz_v<CPR, C::SHARED>(row)) << 4)) = vv;
+        }
       }
     }
   };

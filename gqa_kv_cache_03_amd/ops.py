@@ -297,8 +297,27 @@ def gqla_absorb_decode(q, latent_cache, w_uk, w_uv, seq_lens, block_table=None, 
     [G, d_h, d_c]; seq_lens int32 [B]. Returns out [B, q_len, H, d_h]: attention of
     each head over its group's expanded cache W c_j, computed against the latent.
     """
+    return _latent_call(q, None, latent_cache, w_uk, w_uv, seq_lens, block_table, scale=scale, out=out,
+                        causal=causal, num_splits=num_splits, policy=policy, workspace=workspace,
+                        profile_events=profile_events)
+
+
+def gqla_absorb_decode_append(q, c_new, latent_cache, w_uk, w_uv, seq_lens, block_table=None, *,
+                              scale: Optional[float] = None, out=None, causal: bool = True, num_splits: int = 0,
+                              policy: str = "auto", workspace=None, profile_events=None):
+    """gqla_absorb_decode fused with writing the new tokens' latents c_new [B, q_len, d_c]
+    into latent_cache at positions seq_lens[b] - q_len + t (the cache is modified)."""
+    return _latent_call(q, c_new, latent_cache, w_uk, w_uv, seq_lens, block_table, scale=scale, out=out,
+                        causal=causal, num_splits=num_splits, policy=policy, workspace=workspace,
+                        profile_events=profile_events)
+
+
+def _latent_call(q, c_new, latent_cache, w_uk, w_uv, seq_lens, block_table, *, scale, out, causal, num_splits,
+                 policy, workspace, profile_events):
     import torch
     tensors = [("q", q), ("latent_cache", latent_cache), ("w_uk", w_uk), ("w_uv", w_uv), ("seq_lens", seq_lens)]
+    if c_new is not None:
+        tensors.append(("c_new", c_new))
     for name, t in tensors:
         if t is None:
             raise ValueError(f"{name} is required")
@@ -306,7 +325,7 @@ def gqla_absorb_decode(q, latent_cache, w_uk, w_uv, seq_lens, block_table=None, 
             raise ValueError(f"{name} must be a device tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    for name, t in tensors[1:4]:
+    for name, t in tensors[1:4] + tensors[5:]:
         if t.dtype != q.dtype:
             raise TypeError(f"{name} must have q's dtype")
     if w_uv.shape != w_uk.shape:
@@ -319,6 +338,8 @@ def gqla_absorb_decode(q, latent_cache, w_uk, w_uv, seq_lens, block_table=None, 
     B, q_len, H, d_h, G, d_c, geo = _latent_geometry(q, latent_cache, w_uk, block_table)
     if seq_lens.numel() != B:
         raise ValueError("seq_lens must have B entries")
+    if c_new is not None and tuple(c_new.shape) != (B, q_len, d_c):
+        raise ValueError("c_new must be [B, q_len, d_c]")
     if scale is None:
         scale = 1.0 / math.sqrt(d_h)
     o = make_opts(dtype_code=_dtype_code(torch, q.dtype), causal=causal, num_splits=num_splits, policy=policy,
@@ -341,9 +362,16 @@ def gqla_absorb_decode(q, latent_cache, w_uk, w_uv, seq_lens, block_table=None, 
             o.profile_events[i] = ev
     stream = torch.cuda.current_stream(q.device).cuda_stream
     bt = None if block_table is None else block_table.data_ptr()
-    st = L.gqla_absorb_decode(q.data_ptr(), latent_cache.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
-                              seq_lens.data_ptr(), bt, out.data_ptr(), B, H, G, d_h, d_c, q_len,
-                              ctypes.c_float(scale), stream, ctypes.byref(o))
+    if c_new is None:
+        st = L.gqla_absorb_decode(q.data_ptr(), latent_cache.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+                                  seq_lens.data_ptr(), bt, out.data_ptr(), B, H, G, d_h, d_c, q_len,
+                                  ctypes.c_float(scale), stream, ctypes.byref(o))
+        what = "gqla_absorb_decode"
+    else:
+        st = L.gqla_absorb_decode_append(q.data_ptr(), c_new.data_ptr(), w_uk.data_ptr(), w_uv.data_ptr(),
+                                         latent_cache.data_ptr(), seq_lens.data_ptr(), bt, out.data_ptr(), B, H,
+                                         G, d_h, d_c, q_len, ctypes.c_float(scale), stream, ctypes.byref(o))
+        what = "gqla_absorb_decode_append"
     if st != _lib.GQA_OK:
-        raise GqaError(st, "gqla_absorb_decode")
+        raise GqaError(st, what)
     return out

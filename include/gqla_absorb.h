@@ -75,6 +75,30 @@ int gqla_absorb_decode(const void* q, const void* latent_cache, const void* w_uk
                        int B, int H, int G, int d_h, int d_c, int q_len, float scale,
                        void* stream, const gqa_decode_opts* opts);
 
+/*
+ * gqla_absorb_decode_append -- the same absorbed decode step, fused with writing the
+ * q_len new tokens' latents into the latent cache (asynchronous on `stream`). Every
+ * cached token keeps one joint latent vector (the GQLA abstract), so a decode step adds
+ * one latent row per new token, and then attends over the whole cache.
+ *
+ *   c_new        bf16 [B, q_len, d_c]: the new tokens' latents, row t of sequence b
+ *                being cache position seq_lens[b] - q_len + t.
+ *   latent_cache written at those positions (contiguous: [b, pos]; paged: page
+ *                block_table[b][pos / P], slot pos % P, which the caller has allocated),
+ *                read everywhere else; no other cache byte is written.
+ *   Everything else is as for gqla_absorb_decode, whose result this equals when called
+ *   on the cache after the append.
+ *
+ * The new rows are read straight from c_new by the latent attention kernel, which also
+ * copies them into the cache from LDS: the launches are those of gqla_absorb_decode.
+ * c_new must be 16-byte aligned and must not alias the cache or out. Errors are those
+ * of gqla_absorb_decode plus INVALID_ARGUMENT for a NULL or misaligned c_new.
+ */
+int gqla_absorb_decode_append(const void* q, const void* c_new, const void* w_uk, const void* w_uv,
+                              void* latent_cache, const int32_t* seq_lens, const int32_t* block_table,
+                              void* out, int B, int H, int G, int d_h, int d_c, int q_len, float scale,
+                              void* stream, const gqa_decode_opts* opts);
+
 /* The plan of the latent attention kernel gqla_absorb_decode would launch (rows =
  * H * q_len: every query head reads the one latent), with workspace_bytes covering the
  * whole call. Set opts->page_size > 0 for a paged latent. */

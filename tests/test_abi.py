@@ -397,3 +397,20 @@ def test_check_inputs_rejects_bad_arguments(kw, status):
     elif isinstance(o, dict):
         o = opts(**o)
     assert ccall(o=o, **kw) == status
+
+
+def lacall(cn=P, B=2, H=16, G=2, d=128, d_c=512, q_len=1, o=None, q=P, lat=P, wk=P, wv=P, sl=P, bt=None, out=P):
+    o = opts() if o is None else o
+    return _lib.lib().gqla_absorb_decode_append(q, cn, wk, wv, lat, sl, bt, out, B, H, G, d, d_c, q_len,
+                                                ctypes.c_float(0.1), None, ctypes.byref(o))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cn=None), INV), (dict(cn=P + 8), INV), (dict(lat=None), INV), (dict(q=P + 4), INV),
+    (dict(d_c=256), UNS), (dict(H=16, G=3), INV),
+    (dict(), WS),                                  # every argument valid: only the workspace is missing
+])
+def test_latent_append_rejects_bad_arguments(kw, status):
+    """gqla_absorb_decode_append checks what gqla_absorb_decode checks, plus c_new,
+    on the host before any HIP call."""
+    assert lacall(**kw) == status
