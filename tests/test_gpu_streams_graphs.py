@@ -2,11 +2,12 @@
 
 - A call issued on a side stream gives the same bits as one on the default stream
   (the persistent schedule is deterministic: no atomics, a fixed combine order).
-- gqa_decode and gqla_absorb_decode captured once in a graph (workspace and output
-  allocated beforehand; the library allocates nothing and records no memset) give, on
-  every replay, the bits an eager call gives for the inputs current at that replay:
-  the queries are rewritten in place between replays, with eager work and
-  synchronisations in between.
+- gqa_decode, gqa_decode_noalloc and gqla_absorb_decode captured once in a graph
+  (workspace and output allocated beforehand; the library allocates nothing and records
+  no memset) give, on every replay, the bits an eager call gives for the inputs current
+  at that replay: the queries are rewritten in place between replays, with eager work
+  and synchronisations in between.
+- gqa_decode_check_inputs captured once reports afresh on every replay.
 """
 import numpy as np
 import pytest
@@ -91,3 +92,64 @@ def test_graph_replays_gqla_absorb_decode():
         ref = gqla_absorb_decode(*args, scale=wl.scale)
         torch.cuda.synchronize()
         assert torch.equal(got, ref), f"replay {rep}"
+
+
+def test_graph_replays_gqa_decode_noalloc():
+    """The no-allocation entry point captured in a graph (the use it exists for): every
+    replay gives the bits of an eager gqa_decode on the inputs current at that replay."""
+    from gqa_kv_cache_03_amd import gqa_decode, gqa_decode_noalloc
+    wl, lens = small_workload(4, 32, 4, 128, 2, [700, 64, 2500, 1300], paged=32, seed=6400)
+    inp = make(wl, lens)
+    out = torch.empty_like(inp.q)
+    args = (inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table)
+    gqa_decode_noalloc(*args, scale=wl.scale, out=out)   # warm-up: looks up the scratch address
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gqa_decode_noalloc(*args, scale=wl.scale, out=out)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(6401)
+    for rep in range(4):
+        inp.q.copy_(torch.randn(inp.q.shape, generator=gen, device="cuda").to(inp.q.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = gqa_decode(*args, scale=wl.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), f"replay {rep}"
+
+
+def test_graph_replays_check_inputs():
+    """gqa_decode_check_inputs clears its report with a kernel, so a captured call reports
+    afresh on every replay: the lengths are changed in place between replays."""
+    import ctypes
+
+    from gqa_kv_cache_03_amd import _lib
+    lens = torch.tensor([5, 64, 17], dtype=torch.int32, device="cuda")
+    report = torch.full((4,), -5, dtype=torch.int32, device="cuda")
+    o = _lib.default_opts()
+    o.cache_capacity = 64
+
+    def call():
+        st = _lib.lib().gqa_decode_check_inputs(lens.data_ptr(), None, 3, 2,
+                                                torch.cuda.current_stream().cuda_stream, ctypes.byref(o),
+                                                report.data_ptr())
+        assert st == _lib.GQA_OK
+
+    call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    none = 2 ** 31 - 1
+    for new_lens, expect in [([5, 64, 17], [0, 0, none, none]),
+                             ([1, 65, 17], [2, 0, 0, none]),
+                             ([5, 64, 0], [1, 0, 2, none]),
+                             ([2, 2, 64], [0, 0, none, none])]:
+        lens.copy_(torch.tensor(new_lens, dtype=torch.int32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert report.cpu().tolist() == expect, new_lens
