@@ -6,7 +6,8 @@ batch, heads, groups, head width, new tokens, ragged lengths, contiguous or page
 fp32, either kernel policy.
 The point is to cross the plans' decision boundaries at combinations no hand-written
 case names: row blocks, policies, partial-slot layouts, page crossings and ragged
-tails, together.
+tails, together. The fused appends (GQA and GQLA) run on such shapes too, their caches
+checked bit for bit.
 """
 import numpy as np
 import pytest
@@ -94,3 +95,67 @@ def test_random_gqla_shape(seed):
     else:
         ref = oracle.gqla_decode(host64(inp.q), host64(inp.latent), wk, wv, lens, wl.scale, causal=causal)
     assert_parity(host64(out), ref, "bfloat16", f"gqla seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_random_gqa_append_shape(seed):
+    """The fused append on the same kind of random shapes (lengths seven times longer
+    for every other seed): the output and both caches against the oracle."""
+    from gqa_kv_cache_03_amd import gqa_decode_append
+    from test_gpu_append import split_new_rows
+    B, H, G, d, q_len, lens, page, dtype, causal, splits, policy = draw_case(7800 + seed)
+    if seed % 2:
+        lens = [q_len + (L - q_len) * 7 for L in lens]
+    wl, lens = small_workload(B, H, G, d, q_len, lens, dtype=dtype, paged=page, seed=7900 + seed, causal=causal)
+    inp = make(wl, lens)
+    k_new, v_new = split_new_rows(inp)
+    tbl = None if inp.table is None else inp.table.astype(np.int64)
+    exp_k = oracle.append_kv(host64(inp.k_cache), host64(k_new), inp.lens, tbl, wl.page_size)
+    exp_v = oracle.append_kv(host64(inp.v_cache), host64(v_new), inp.lens, tbl, wl.page_size)
+    print(f"[random append] seed={seed} B={B} H={H} G={G} d={d} q_len={q_len} page={page} {dtype} "
+          f"causal={causal} splits={splits} policy={policy} lens={list(lens)}", flush=True)
+    out = gqa_decode_append(inp.q, k_new, v_new, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table,
+                            scale=wl.scale, causal=causal, num_splits=splits, policy=policy)
+    torch.cuda.synchronize()
+    for got, exp in ((host64(inp.k_cache), exp_k), (host64(inp.v_cache), exp_v)):
+        np.testing.assert_array_equal(np.isnan(got), np.isnan(exp))
+        np.testing.assert_array_equal(np.nan_to_num(got), np.nan_to_num(exp))
+    ref = oracle.gqa_decode(host64(inp.q), exp_k, exp_v, inp.lens, wl.scale, wl.G, block_table=tbl,
+                            page_size=wl.page_size, causal=causal)
+    assert_parity(host64(out), ref, dtype, f"append seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_gqla_append_shape(seed):
+    """The fused latent append on random GQLA shapes: output and latent cache against the
+    oracle."""
+    from gqa_kv_cache_03_amd import gqla_absorb_decode_append
+    from test_gpu_gqla_append import split_new_latents
+    rng = np.random.default_rng(7700 + seed)
+    G = int(rng.choice([1, 2, 4]))
+    H = G * int(rng.choice([1, 4, 8, 16]))
+    q_len = int(rng.choice([1, 2, 3, 4]))
+    B = int(rng.integers(1, 5))
+    d = int(rng.choice([64, 128]))
+    lens = np.array([int(rng.integers(q_len, 900)) for _ in range(B)], dtype=np.int32)
+    page = int(rng.choice([0, 16, 32]))
+    causal = bool(rng.random() < 0.8)
+    splits = int(rng.choice([0, 1, 9, 200]))
+    wl = Workload(name=f"t_rand_gqla_app_{seed}", B=B, H=H, G=G, d_h=d, q_len=q_len, dtype="bfloat16",
+                  len_lo=int(lens.min()), len_hi=int(lens.max()), layout="paged" if page else "contiguous",
+                  page_size=page, causal=causal, seed=7750 + seed, extra_pages=2 if page else 0, d_c=512)
+    inp = make_latent_inputs(wl, device="cuda", lens=lens)
+    c_new = split_new_latents(inp)
+    tbl = None if inp.table is None else inp.table.astype(np.int64)
+    exp = oracle.append_latent(host64(inp.latent), host64(c_new), inp.lens, tbl, page)
+    print(f"[random gqla append] seed={seed} B={B} H={H} G={G} d={d} q_len={q_len} page={page} "
+          f"causal={causal} splits={splits} lens={list(lens)}", flush=True)
+    out = gqla_absorb_decode_append(inp.q, c_new, inp.latent, inp.w_uk, inp.w_uv, inp.seq_lens, inp.block_table,
+                                    scale=wl.scale, causal=causal, num_splits=splits)
+    torch.cuda.synchronize()
+    got = host64(inp.latent)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(exp))
+    np.testing.assert_array_equal(np.nan_to_num(got), np.nan_to_num(exp))
+    ref = oracle.gqla_decode(host64(inp.q), exp, host64(inp.w_uk), host64(inp.w_uv), inp.lens, wl.scale,
+                             block_table=tbl, page_size=page, causal=causal)
+    assert_parity(host64(out), ref, "bfloat16", f"gqla append seed {seed}")
