@@ -44,3 +44,30 @@ def test_full_size_parity_every_unit(name):
     assert worst["units"] == wl.B * wl.G
     del inp, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_decode_bf16_B16_H32_G8_d128_n4096",
+                                  "paged16_bf16_B64_H32_G4_d128_n8k_64k",
+                                  "causal4_bf16_B8_H32_G1_d128_n131072p4"])
+def test_full_size_append_every_unit(name):
+    """The fused append at full size, default plan: the new tokens' K/V come from k_new /
+    v_new (their cache slots hold NaN on entry). Afterwards the cache equals the generated
+    one bit for bit, and every (sequence, group) unit of the output matches the oracle
+    over it."""
+    from gqa_kv_cache_03_amd import gqa_decode_append
+    from test_gpu_append import split_new_rows
+    wl = WORKLOADS[name]
+    _log(f"[fullsize append] {name}: generating")
+    inp = make_inputs(wl, device="cuda")
+    full_k, full_v = inp.k_cache.clone(), inp.v_cache.clone()
+    k_new, v_new = split_new_rows(inp)
+    out = gqa_decode_append(inp.q, k_new, v_new, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table,
+                            scale=wl.scale, causal=wl.causal)
+    torch.cuda.synchronize()
+    assert torch.equal(inp.k_cache.view(torch.int16), full_k.view(torch.int16)), "K cache bytes"
+    assert torch.equal(inp.v_cache.view(torch.int16), full_v.view(torch.int16)), "V cache bytes"
+    del full_k, full_v
+    worst = all_units_parity(inp, out, name + " +append", log=_log)
+    assert worst["units"] == wl.B * wl.G
+    del inp, out
+    torch.cuda.empty_cache()

@@ -190,6 +190,47 @@ def test_full_size_parity_every_sequence():
                   f"rel_l2 {e['rel_l2']:.2e}", flush=True)
 
 
+def test_full_size_latent_append():
+    """The fused latent append on the benchmark's GQLA workload at full size: afterwards
+    the latent pool equals the generated one bit for bit, and every sequence of the
+    output matches the oracle over it (the oracle on host threads, as above)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    from gpu_cases import host_workers
+    from gqa_kv_cache_03_amd import gqla_absorb_decode_append
+    from test_gpu_gqla_append import split_new_latents
+    wl = workload("gqla_absorb_tp8_bf16_B16_H16_G2_d128_c512_n8k_64k")
+    print(f"[gqla append] {wl.name}: generating", flush=True)
+    inp = make_latent_inputs(wl, device="cuda")
+    full = inp.latent.clone()
+    c_new = split_new_latents(inp)
+    out = gqla_absorb_decode_append(inp.q, c_new, inp.latent, inp.w_uk, inp.w_uv, inp.seq_lens, inp.block_table,
+                                    scale=wl.scale, causal=wl.causal)
+    torch.cuda.synchronize()
+    assert torch.equal(inp.latent.view(torch.int16), full.view(torch.int16)), "latent cache bytes"
+    del full
+    got = host64(out)
+    wk, wv = host64(inp.w_uk), host64(inp.w_uv)
+    P = wl.page_size
+
+    def one(b, q, lat):
+        ref = oracle.gqla_decode(q, lat, wk, wv, inp.lens[b:b + 1], wl.scale, causal=wl.causal)
+        return b, assert_parity(got[b:b + 1], ref, "bfloat16", f"{wl.name} +append b={b}")
+
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=host_workers()) as ex:
+        futs = []
+        for b in range(wl.B):
+            L = int(inp.lens[b])
+            n = -(-L // P)
+            pages = torch.as_tensor(inp.table[b, :n].astype(np.int64), device=inp.latent.device)
+            lat = host64(inp.latent[pages].reshape(1, n * P, wl.d_c)[:, :L])
+            futs.append(ex.submit(one, b, host64(inp.q[b:b + 1]), lat))
+        for f in futs:
+            f.result()
+
+
 @pytest.mark.parametrize("splits", [0, 37])
 def test_many_sequences(splits):
     """More than 64 sequences (several chunks of the schedule scan), ragged, paged."""
