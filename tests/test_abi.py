@@ -414,3 +414,16 @@ def test_latent_append_rejects_bad_arguments(kw, status):
     """gqla_absorb_decode_append checks what gqla_absorb_decode checks, plus c_new,
     on the host before any HIP call."""
     assert lacall(**kw) == status
+
+
+def test_plain_c_client(tmp_path):
+    """The public headers are plain C: a C program compiles against include/ alone, links
+    against the library and gets the host-side results the Python binding gets."""
+    lib_dir = os.path.dirname(_lib.LIB_PATH)
+    exe = tmp_path / "c_client"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c_client.c"), "-L", lib_dir, "-lgqa_decode",
+                    f"-Wl,-rpath,{lib_dir}", "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.count("ok ") == 12
