@@ -63,6 +63,9 @@ CASES = [
     (2, 16, 2, 64, 16, [300, 17], "float32", 32),      # fp32, q_len 16, paged 32, L ~ q_len
     (3, 8, 8, 128, 1, [1, 2, 3], "bfloat16", 0),       # MHA, R = 1, tiny sequences
     (2, 64, 8, 128, 1, [131, 32768], "bfloat16", 0),   # one long, one short sequence
+    (1, 64, 1, 128, 16, [700], "bfloat16", 0),         # R = 1024, the most rows a group may pack: 8 blocks
+    (1, 64, 1, 64, 16, [300], "bfloat16", 256),        # R = 1024, d = 64, the largest page (256)
+    (2, 32, 4, 128, 1, [5000, 300], "bfloat16", 128),  # paged 128
 ]
 
 
@@ -126,7 +129,7 @@ def test_split_invariance_fp32_tight():
         assert np.abs(o - base).max() <= 1e-6 * max(1.0, np.abs(base).max())
 
 
-@pytest.mark.parametrize("page", [16, 32, 64])
+@pytest.mark.parametrize("page", [16, 32, 64, 128, 256])
 def test_paged_equals_contiguous(page):
     """Same keys in a permuted pool: bitwise-equal output for the same split plan."""
     from gqa_synth.generate import paginate
