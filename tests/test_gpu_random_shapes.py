@@ -7,7 +7,8 @@ fp32, either kernel policy.
 The point is to cross the plans' decision boundaries at combinations no hand-written
 case names: row blocks, policies, partial-slot layouts, page crossings and ragged
 tails, together. The fused appends (GQA and GQLA) run on such shapes too, their caches
-checked bit for bit.
+checked bit for bit. A few larger draws (up to 130 sequences, contexts up to 20k
+tokens, pages up to 256) are checked on every (sequence, group) unit.
 """
 import numpy as np
 import pytest
@@ -15,7 +16,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
-from gpu_cases import assert_parity, host64, make, oracle_for, small_workload  # noqa: E402
+from gpu_cases import all_units_parity, assert_parity, host64, make, oracle_for, small_workload  # noqa: E402
 from gqa_synth import Workload, make_latent_inputs  # noqa: E402
 
 pytestmark = pytest.mark.gpu
@@ -63,6 +64,44 @@ def test_random_gqa_shape(seed):
                      causal=causal, num_splits=splits, policy=policy)
     torch.cuda.synchronize()
     assert_parity(host64(out), oracle_for(inp, causal=causal), dtype, f"seed {seed}")
+
+
+def draw_large_case(seed):
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    hpg = int(rng.choice([1, 2, 4, 8, 16, 32, 64]))
+    if G * hpg > 256:
+        hpg = max(1, 256 // G)
+    H = G * hpg
+    q_len = int(rng.choice([1, 1, 2, 4, 8, 16]))
+    while hpg * q_len > 1024:
+        q_len //= 2
+    d = int(rng.choice([64, 128]))
+    B = int(rng.choice([1, 3, 17, 65, 130]))
+    l_max = int(rng.choice([300, 3000, 20000]))
+    if B * G * l_max > 40_000_000:  # at most 40M cached rows per tensor
+        l_max = max(q_len + 1, 40_000_000 // (B * G))
+    lens = [int(rng.integers(q_len, max(q_len + 1, l_max))) for _ in range(B)]
+    page = int(rng.choice([0, 16, 32, 64, 128, 256]))
+    causal = bool(rng.random() < 0.8)
+    splits = int(rng.choice([0, 0, 0, 1, 13, 1000]))
+    return B, H, G, d, q_len, lens, page, causal, splits
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_large_gqa_shape(seed):
+    from gqa_kv_cache_03_amd import gqa_decode
+    B, H, G, d, q_len, lens, page, causal, splits = draw_large_case(50000 + seed)
+    wl, lens = small_workload(B, H, G, d, q_len, lens, dtype="bfloat16", paged=page, seed=50000 + seed,
+                              causal=causal)
+    inp = make(wl, lens)
+    print(f"[random large] seed={seed} B={B} H={H} G={G} d={d} q_len={q_len} page={page} causal={causal} "
+          f"splits={splits} max L={max(lens)}", flush=True)
+    out = gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table, scale=wl.scale,
+                     causal=causal, num_splits=splits)
+    torch.cuda.synchronize()
+    worst = all_units_parity(inp, out, f"large seed {seed}", log=lambda m: None)
+    assert worst["units"] == B * G
 
 
 @pytest.mark.parametrize("seed", range(12))
