@@ -217,6 +217,20 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     voff[kp] = (uint32_t)(rl * ROW_BYTES + ((pch ^ swz_v<CPR, C::SHARED>(row)) << 4));
   }
 
+  // Block-table entries of the next tile to issue, one per 16 rows (pages hold at
+  // least 16 rows), loaded one pipeline step early so that the scalar loads' latency
+  // overlaps the current tile's work instead of delaying the next tile's loads.
+  int pf[T / 16] = {};
+  auto prefetch_pages = [&](const Cursor& c) {
+    if constexpr (PAGED) {
+      if (c.b < p.B) {
+        const int32_t* trow = p.table + (size_t)c.b * p.max_blocks;
+        const int t0 = c.t * T;
+#pragma unroll
+        for (int gi = 0; gi < T / 16; ++gi) pf[gi] = load_uniform_i32(trow, min(t0 + gi * 16, c.L - 1) >> pshift);
+      }
+    }
+  };
   auto issue_tile = [&](const Cursor& c, int f) {
     unsigned char* st = smem + (f % NS) * C::STAGE_BYTES;
     const int t0 = c.t * T;
@@ -231,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         const int j0 = t0 + n * C::RPL;  // first row of this load
         size_t rb;
         if constexpr (PAGED) {
-          int page = load_uniform_i32(p.table + (size_t)c.b * p.max_blocks, j0 >> pshift);
+          int page = pf[(n * C::RPL) >> 4];
           page = page < 0 ? 0 : (page >= p.num_pages ? p.num_pages - 1 : page);
           rb = (((size_t)page * p.G + c.g) * (size_t)(pmask + 1) + (j0 & pmask)) * ROW_BYTES;
         } else {
@@ -661,11 +675,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   // full wait covers both, so no wait for the query registers is left in the loop.
   {
     Cursor c = issue;
+    prefetch_pages(c);
 #pragma unroll
     for (int f = 0; f < AHEAD; ++f) {
       if (f < count) {
         issue_tile(c, f);
         advance(c);
+        prefetch_pages(c);
       }
     }
     issue = c;
@@ -702,6 +718,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     if (f + AHEAD < count) {
       issue_tile(issue, f + AHEAD);
       advance(issue);
+      prefetch_pages(issue);
     }
     const int tile0 = cons.t * T;
     const bool masked = tile0 + T - 1 > lim_min;

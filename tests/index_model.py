@@ -10,8 +10,11 @@ would only show as a fault or a silently wrong row:
 
 * every (sequence, group, row block, tile) is consumed by exactly one workgroup;
 * every cache row, block-table entry and page a tile touches lies inside its buffer
-  (only the table entries below ceil(L / P) are read, as the header promises);
-* a plain-path staging load never straddles a page;
+  (only the table entries below ceil(L / P) are read, as the header promises), the
+  entries of the tile after a workgroup's last one included (they are loaded one
+  pipeline step ahead);
+* a plain-path staging load never straddles a page, and the entry loaded ahead for
+  its 16-row group is its page;
 * every partial row a workgroup writes lies inside the workspace the plan sizes, no
   (workgroup, slot) is written twice, and only a segment cut by a workgroup boundary
   writes one;
@@ -162,9 +165,14 @@ def check_persistent(shape: Shape, plan: dict) -> Report:
             fast = L // T_MFMA
             if P >= RPL and t_first < fast:
                 for n_ld in range(T_MFMA * CPR // 256):
-                    j0 = t_first * T_MFMA + n_ld * RPL
+                    t0 = t_first * T_MFMA
+                    j0 = t0 + n_ld * RPL
                     _check((j0 >> pshift) == ((j0 + RPL - 1) >> pshift), "staging load straddles a page")
                     _check(j0 + RPL - 1 < L, "plain-path load past the end")
+                    # the plain path takes the page of load n_ld from the prefetched entry
+                    # of its 16-row group
+                    _check((j0 >> pshift) == ((t0 + 16 * ((n_ld * RPL) >> 4)) >> pshift),
+                           "prefetched entry is not the load's page")
         else:
             row = (b * shape.G + g) * shape.capacity + j_max
             _check(j_max < shape.capacity and row < shape.B * shape.G * shape.capacity,
@@ -206,6 +214,9 @@ def check_persistent(shape: Shape, plan: dict) -> Report:
                     rep.max_ws_row = max(rep.max_ws_row, prow)
                 rep.partial_writes += 1
             first = False
+            if not seg_end:   # the workgroup's last tile ends inside this segment
+                t += take
+                break
             # advance: next segment of b, else next sequence
             t = 0
             seg_from_start = True
@@ -213,6 +224,15 @@ def check_persistent(shape: Shape, plan: dict) -> Report:
             if seg == GS:
                 seg = 0
                 b += 1
+        # paged: the table entries of the tile after the workgroup's last one are loaded
+        # ahead (the cursor stops there); that tile belongs to another workgroup's share
+        if paged and b < shape.B:
+            L = lens[b]
+            _check(t < seg_tiles(b), "look-ahead tile outside its segment")
+            for gi in range(T_MFMA // 16):
+                idx = min(t * T_MFMA + 16 * gi, L - 1) >> pshift
+                _check(idx < (L + P - 1) // P and idx < shape.max_blocks, "look-ahead table entry out of range")
+                rep.max_table_index = max(rep.max_table_index, idx)
     _check(rep.tiles == W, f"consumed {rep.tiles} of {W} tiles")
     slots = [ws for v in written.values() for ws in v]
     _check(len(slots) == len(set(slots)), "a (workgroup, slot) written twice")
