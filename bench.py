@@ -405,6 +405,14 @@ def measure(name, args, dev, variant_opts=True, ceiling=False):
                 ceilings=ceilings)
 
 
+def decode_kernel_name(pl) -> str:
+    """The decode kernel a plan launches: the matrix-core kernel (its re-reading form
+    when the group's rows are split into row blocks) or the vector-ALU kernel."""
+    if pl["policy"] != "mfma":
+        return "decode_valu_kernel"
+    return "decode_mfma_reread_kernel" if pl["row_blocks"] > 1 else "decode_mfma_kernel"
+
+
 def roofline_of(m, traffic_key):
     """The dominant (decode) kernel against the roofline that bounds it."""
     mb = m["mfma_bound"]
@@ -415,7 +423,7 @@ def roofline_of(m, traffic_key):
         "unit": "TFLOP/s" if mb else "GB/s",
         "frac": round(m["tflops"] / MFMA_BF16_PEAK_TFLOPS if mb else m["achieved"] / HBM_PEAK_GBPS, 4),
         "traffic": load_traffic(traffic_key) if not m["variant"] else None,
-        "kernel": "decode_mfma_kernel" if m["pl"]["policy"] == "mfma" else "decode_valu_kernel",
+        "kernel": decode_kernel_name(m["pl"]),
         "algorithmic_bytes_per_launch": int(m["dec_alg_bytes"]),
         "flops_per_launch": int(m["flops"]),
         "flop_per_byte": round(m["intensity"], 2),

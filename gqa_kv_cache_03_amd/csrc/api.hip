@@ -160,8 +160,9 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
     // (for the 64/128-wide kernels): their variant leaves room for two workgroups per
     // CU, which measured faster than half as many 256-row blocks. Each block reads the
     // group's K/V once more, but the blocks of a group are neighbours in the schedule
-    // and stream the same tiles at about the same time, so the caches serve most of
-    // the repeats (four blocks of 512 rows: 1.13x the single-read bytes from HBM).
+    // and stream the same tiles at about the same time, and their kernel loads with the
+    // default cache policy, so L2 serves most of the repeats (four blocks of 512 rows:
+    // 1.06x the single-read bytes from HBM).
     int block_rows = gqa::mfma_max_rows(d_h);
     if (R > block_rows && d_h != kLatentWidth) block_rows = kSplitBlockRows;
     const int n_rb = (int)((R + block_rows - 1) / block_rows);

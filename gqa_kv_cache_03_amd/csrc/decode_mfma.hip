@@ -106,9 +106,16 @@ struct Cursor {
   uint64_t base;
 };
 
-template <int D, int NRW, int NCW, int RTW, bool PAGED>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+// REREAD: the group's rows are split into row blocks, so every K/V tile is staged once
+// per block. The blocks of a group are neighbours in the schedule and stream the same
+// tiles at about the same time; the default cache policy then lets L2 serve the
+// repeats. A single block keeps nontemporal loads (its tiles are never read again).
+// The two policies are two kernels (decode_mfma_kernel, decode_mfma_reread_kernel
+// below), so neither carries a branch for the other.
+template <int D, int NRW, int NCW, int RTW, bool PAGED, bool REREAD>
+__device__ __forceinline__ void decode_mfma_body(DecodeParams p) {
   using C = MfmaCfg<D, NRW, NCW, RTW>;
+  constexpr int kPolicy = REREAD ? 0 : kNontemporal;
   constexpr int T = C::T, NS = C::NS, AHEAD = C::AHEAD, KB = C::KB, CBW = C::CBW;
   constexpr int CPR = C::CPR, LOADS = C::LOADS, LD = C::LD, ROW_BYTES = C::ROW_BYTES;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS_BYTES];
@@ -252,8 +259,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
           rb = c.base + (uint64_t)(uint32_t)j0 * ROW_BYTES;
         }
         const int lds_off = n * kThreads * 16 + wave * 1024;  // this wave's 64 x 16 B slots
-        load16_to_lds(kg + rb + koff[n % C::KP], st + lds_off);
-        if constexpr (!C::SHARED) load16_to_lds(vg + rb + voff[n % C::KP], st + C::TENSOR_BYTES + lds_off);
+        load16_to_lds<kPolicy>(kg + rb + koff[n % C::KP], st + lds_off);
+        if constexpr (!C::SHARED)
+          load16_to_lds<kPolicy>(vg + rb + voff[n % C::KP], st + C::TENSOR_BYTES + lds_off);
       }
       return;
     }
@@ -276,9 +284,9 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
         }
       }
       const int lds_off = n * kThreads * 16 + wave * 1024;  // this wave's 64 x 16 B slots
-      load16_to_lds(ksrc + ((pch ^ swz_k<CPR, C::SHARED>(row)) << 4), st + lds_off);
+      load16_to_lds<kPolicy>(ksrc + ((pch ^ swz_k<CPR, C::SHARED>(row)) << 4), st + lds_off);
       if constexpr (!C::SHARED)
-        load16_to_lds(vsrc + ((pch ^ swz_v<CPR, C::SHARED>(row)) << 4), st + C::TENSOR_BYTES + lds_off);
+        load16_to_lds<kPolicy>(vsrc + ((pch ^ swz_v<CPR, C::SHARED>(row)) << 4), st + C::TENSOR_BYTES + lds_off);
     }
   };
 
@@ -733,10 +741,34 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   }
 }
 
+template <int D, int NRW, int NCW, int RTW, bool PAGED>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+  decode_mfma_body<D, NRW, NCW, RTW, PAGED, false>(p);
+}
+
+template <int D, int NRW, int NCW, int RTW, bool PAGED>
+__global__ __launch_bounds__(kThreads) void decode_mfma_reread_kernel(DecodeParams p) {
+  decode_mfma_body<D, NRW, NCW, RTW, PAGED, true>(p);
+}
+
+// The layouts a group split into row blocks runs on (blocks of at most 128 rows, or 32
+// in the latent), which alone get the re-reading kernel.
+template <int D, int NRW, int NCW, int RTW>
+constexpr bool kRowBlockLayout = D == 512 ? (NRW == 2 && NCW == 2) : (NRW == 4 && RTW == 2);
+
 template <int D, int NRW, int NCW, int RTW>
 hipError_t launch_variant(const DecodeParams& p, bool paged, dim3 grid, hipStream_t stream, hipEvent_t start,
                           hipEvent_t stop) {
   static_assert(kThreads == 256, "launch_timed launches 256 threads");
+  if constexpr (kRowBlockLayout<D, NRW, NCW, RTW>) {
+    if (p.n_row_blocks > 1) {
+      if (paged)
+        launch_timed(decode_mfma_reread_kernel<D, NRW, NCW, RTW, true>, grid, stream, start, stop, p);
+      else
+        launch_timed(decode_mfma_reread_kernel<D, NRW, NCW, RTW, false>, grid, stream, start, stop, p);
+      return hipGetLastError();
+    }
+  }
   if (paged)
     launch_timed(decode_mfma_kernel<D, NRW, NCW, RTW, true>, grid, stream, start, stop, p);
   else

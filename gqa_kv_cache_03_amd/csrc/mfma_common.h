@@ -112,12 +112,14 @@ __device__ __forceinline__ int swz_v(int row) {
   else return (row << 1) & (CPR - 2);
 }
 
-// One 16-byte direct global->LDS load per lane (nontemporal): lane i of the wave
-// writes LDS bytes [lds_wave_base + 16 i, +16). Device-only: the host pass of this
-// translation unit must not see the builtin (it would drop the kernel stubs).
+// One 16-byte direct global->LDS load per lane (nontemporal unless POLICY says
+// otherwise): lane i of the wave writes LDS bytes [lds_wave_base + 16 i, +16).
+// Device-only: the host pass of this translation unit must not see the builtin (it
+// would drop the kernel stubs).
+template <int POLICY = kNontemporal>
 __device__ __forceinline__ void load16_to_lds(const unsigned char* src, unsigned char* lds_wave_base) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)lds_wave_base, 16, 0, kNontemporal);
+  __builtin_amdgcn_global_load_lds(src, (LDS_AS void*)lds_wave_base, 16, 0, POLICY);
 #else
   (void)src;
   (void)lds_wave_base;

@@ -50,3 +50,10 @@ def test_per_config_entry_reads_a_child_line():
     assert e == {"step_us": 110.5, "kv_gbps": 4860.0, "pct_of_hbm_peak": 60.75, "tokens_per_s": 289592.8,
                  "decode_us": 101.2, "merge_us": 8.3, "decode_roofline_frac": 0.6633, "roofline_bound": "hbm",
                  "traffic": None}
+
+
+def test_decode_kernel_name_follows_the_plan():
+    # a group split into row blocks runs the re-reading form of the matrix-core kernel
+    assert bench.decode_kernel_name({"policy": "mfma", "row_blocks": 1}) == "decode_mfma_kernel"
+    assert bench.decode_kernel_name({"policy": "mfma", "row_blocks": 4}) == "decode_mfma_reread_kernel"
+    assert bench.decode_kernel_name({"policy": "valu", "row_blocks": 1}) == "decode_valu_kernel"
