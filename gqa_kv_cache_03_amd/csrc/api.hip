@@ -330,7 +330,10 @@ int decode_impl(const void* q, const void* k_new, const void* v_new, const void*
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(const_cast<void**>(opts->profile_events));
   const dim3 grid(pl.grid[0], pl.grid[1], pl.grid[2]);
-  if (opts->head_group && gqa::launch_fill_unmapped(dp, d_h, s) != hipSuccess) return GQA_ERR_HIP;
+  // the persistent merge fills a head map's unmapped rows itself; the split-K path
+  // launches the fill on its own
+  if (opts->head_group && pl.policy != GQA_POLICY_MFMA && gqa::launch_fill_unmapped(dp, d_h, s) != hipSuccess)
+    return GQA_ERR_HIP;
   if (k_new && pl.policy != GQA_POLICY_MFMA) {
     // the vector-ALU kernel reads every key from the cache: write the new rows first
     if (gqa::launch_append(dp, opts->dtype == GQA_DTYPE_BF16 ? 2 : 4, d_h, p.paged, s) != hipSuccess)

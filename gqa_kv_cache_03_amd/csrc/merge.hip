@@ -171,6 +171,54 @@ __device__ __forceinline__ void project_up(const DecodeParams& p, const float* s
   if (part == 0) static_cast<__bf16*>(p.proj_out)[orow * dh + i] = (__bf16)acc;
 }
 
+// With a call-time head -> KV head map, the packed tile of KV group g holds the rows
+// r = t * n_g + k (token t, k-th head of the group in ascending order) below
+// cap = n_row_blocks * row_block. A group larger than the planned bound leaves its rows
+// r >= cap uncomputed, and a head whose map entry lies outside [0, G) belongs to no
+// group: the decode kernel never writes those (token, head) rows of `out`. This kernel
+// writes NaN into exactly those rows, so that `out` is always fully overwritten and a
+// bad map shows up in the result. One workgroup per (sequence, token): bt = b * q_len + t.
+// The persistent merge kernels run it in extra workgroups after their own; the split-K
+// path launches it as a kernel of its own.
+__device__ __forceinline__ void fill_unmapped_rows(const DecodeParams& p, int d_h, int bt) {
+  __shared__ int grp[kThreads];
+  __shared__ unsigned char dropped[kThreads];
+  const int tid = threadIdx.x;
+  const int t = bt % p.q_len;
+  if (tid < p.H) grp[tid] = p.head_group[tid];
+  __syncthreads();
+  if (tid < p.H) {
+    const int g = grp[tid];
+    bool drop = g < 0 || g >= p.G;
+    if (!drop) {
+      int k = 0, n_g = 0;
+      for (int h = 0; h < p.H; ++h) {
+        if (grp[h] == g) {
+          k += h < tid;
+          ++n_g;
+        }
+      }
+      drop = t * n_g + k >= p.n_row_blocks * p.row_block;
+    }
+    dropped[tid] = drop ? 1 : 0;
+  }
+  __syncthreads();
+  // the rows to fill, d_h / 4 lanes per head
+  const int lph = d_h / 4;
+  for (int i = tid; i < p.H * lph; i += kThreads) {
+    const int h = i / lph;
+    if (!dropped[h]) continue;
+    const size_t off = ((size_t)bt * p.H + h) * d_h + (i % lph) * 4;
+    put4<__bf16>(static_cast<__bf16*>(p.out) + off, f32x4{__builtin_nanf(""), __builtin_nanf(""),
+                                                          __builtin_nanf(""), __builtin_nanf("")});
+  }
+}
+
+
+__global__ __launch_bounds__(kThreads) void fill_unmapped_rows_kernel(DecodeParams p, int d_h) {
+  fill_unmapped_rows(p, d_h, blockIdx.x);
+}
+
 // One workgroup per (segment, row): D/4 lanes cover the row's D columns and the
 // workgroup's 256 / (D/4) lane groups take the segment's partials in turn, several
 // in flight per lane, each group keeping a running max; the groups then combine
@@ -191,6 +239,13 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_kernel(DecodeParams
 
   const int RB = p.row_block;                     // rows per segment
   const int GS = p.G * p.n_row_blocks;            // segments per sequence
+  if constexpr (D <= 128) {
+    const int merge_blocks = p.B * GS * RB;
+    if ((int)blockIdx.x >= merge_blocks) {  // the head map's unmapped rows
+      fill_unmapped_rows(p, D, blockIdx.x - merge_blocks);
+      return;
+    }
+  }
   const int seg = blockIdx.x / RB;
   const int r_local = blockIdx.x - seg * RB;
   const int b = seg / GS;
@@ -335,6 +390,11 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_wave_kernel(DecodeP
   const int RB = p.row_block;
   const int quads = (RB + 3) / 4;
   const int GS = p.G * p.n_row_blocks;
+  const int merge_blocks = p.B * GS * quads;
+  if ((int)blockIdx.x >= merge_blocks) {  // the head map's unmapped rows
+    fill_unmapped_rows(p, D, blockIdx.x - merge_blocks);
+    return;
+  }
   const int seg = blockIdx.x / quads;
   const int r_local = (blockIdx.x - seg * quads) * 4 + (int)(threadIdx.x >> 6);
   if (r_local >= RB) return;  // the whole wave
@@ -342,10 +402,37 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_wave_kernel(DecodeP
   const int gs = seg - b * GS;
   const int g = gs / p.n_row_blocks;
   const int r = (gs - g * p.n_row_blocks) * RB + r_local;
-  const int n_g = p.hpg;
+  // (token, head) of packed row r as the decode kernel maps it: token r / n_g of the
+  // group's (r % n_g)-th head in ascending order. With a head map the wave finds the
+  // group's heads with one ballot per 64 heads.
+  int n_g = p.hpg;
+  unsigned long long gm[4] = {0ull, 0ull, 0ull, 0ull};
+  if (p.head_group) {
+    n_g = 0;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int hh = ch * 64 + (int)(threadIdx.x & 63);
+      gm[ch] = __builtin_amdgcn_ballot_w64(hh < p.H && p.head_group[hh] == g);
+      n_g += __builtin_popcountll(gm[ch]);
+    }
+  }
   if (r >= n_g * p.q_len) return;
   const int t = r / n_g;
-  const int h = g * n_g + (r - t * n_g);
+  const int kh = r - t * n_g;
+  int h = g * n_g + kh;
+  if (p.head_group) {
+    int before = 0;
+#pragma unroll
+    for (int ch = 0; ch < 4; ++ch) {
+      const int cnt = __builtin_popcountll(gm[ch]);
+      if (kh >= before && kh < before + cnt) {
+        unsigned long long bits = gm[ch];
+        for (int i = before; i < kh; ++i) bits &= bits - 1;  // drop the lower set bits
+        h = ch * 64 + __builtin_ctzll(bits);
+      }
+      before += cnt;
+    }
+  }
   const size_t orow = ((size_t)b * p.q_len + t) * p.H + h;
   const bool on = p.head_active == nullptr || p.head_active[orow] != 0;
 
@@ -420,62 +507,23 @@ __global__ __launch_bounds__(kThreads) void merge_persistent_wave_kernel(DecodeP
 
 template <int D>
 hipError_t go_persistent(const DecodeParams& p, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  // with a head map, one more workgroup per (sequence, token) fills the unmapped rows
+  if (p.head_group && (D > 128 || p.H > kThreads)) return hipErrorInvalidValue;
+  const int fill_blocks = p.head_group ? p.B * p.q_len : 0;
   if constexpr (D <= 128) {
     // A wave takes 4 * (256 / D) partials per round, a workgroup four times as many:
     // the wave form wins while segments average up to two of its rounds of partials
     // (about nwg / segments each), the workgroup form beyond.
     const long long segments = (long long)p.B * p.G * p.n_row_blocks;
-    if (p.head_group == nullptr && p.nwg <= 2 * (4 * (256 / D)) * segments) {
-      const dim3 grid(p.B * p.G * p.n_row_blocks * ((p.row_block + 3) / 4));
+    if (p.nwg <= 2 * (4 * (256 / D)) * segments) {
+      const dim3 grid(p.B * p.G * p.n_row_blocks * ((p.row_block + 3) / 4) + fill_blocks);
       launch_timed(merge_persistent_wave_kernel<D>, grid, stream, start, stop, p);
       return hipGetLastError();
     }
   }
-  const dim3 grid(p.B * p.G * p.n_row_blocks * p.row_block);
+  const dim3 grid(p.B * p.G * p.n_row_blocks * p.row_block + fill_blocks);
   launch_timed(merge_persistent_kernel<D>, grid, stream, start, stop, p);
   return hipGetLastError();
-}
-
-// With a call-time head -> KV head map, the packed tile of KV group g holds the rows
-// r = t * n_g + k (token t, k-th head of the group in ascending order) below
-// cap = n_row_blocks * row_block. A group larger than the planned bound leaves its rows
-// r >= cap uncomputed, and a head whose map entry lies outside [0, G) belongs to no
-// group: the decode kernel never writes those (token, head) rows of `out`. This kernel
-// writes NaN into exactly those rows, so that `out` is always fully overwritten and a
-// bad map shows up in the result. One workgroup per (sequence, token).
-__global__ __launch_bounds__(kThreads) void fill_unmapped_rows_kernel(DecodeParams p, int d_h) {
-  __shared__ int grp[kThreads];
-  __shared__ unsigned char dropped[kThreads];
-  const int tid = threadIdx.x;
-  const int bt = blockIdx.x;  // b * q_len + t
-  const int t = bt % p.q_len;
-  if (tid < p.H) grp[tid] = p.head_group[tid];
-  __syncthreads();
-  if (tid < p.H) {
-    const int g = grp[tid];
-    bool drop = g < 0 || g >= p.G;
-    if (!drop) {
-      int k = 0, n_g = 0;
-      for (int h = 0; h < p.H; ++h) {
-        if (grp[h] == g) {
-          k += h < tid;
-          ++n_g;
-        }
-      }
-      drop = t * n_g + k >= p.n_row_blocks * p.row_block;
-    }
-    dropped[tid] = drop ? 1 : 0;
-  }
-  __syncthreads();
-  // the rows to fill, d_h / 4 lanes per head
-  const int lph = d_h / 4;
-  for (int i = tid; i < p.H * lph; i += kThreads) {
-    const int h = i / lph;
-    if (!dropped[h]) continue;
-    const size_t off = ((size_t)bt * p.H + h) * d_h + (i % lph) * 4;
-    put4<__bf16>(static_cast<__bf16*>(p.out) + off, f32x4{__builtin_nanf(""), __builtin_nanf(""),
-                                                          __builtin_nanf(""), __builtin_nanf("")});
-  }
 }
 
 }  // namespace
