@@ -175,7 +175,7 @@ __device__ __forceinline__ void project_up(const DecodeParams& p, const float* s
 // r = t * n_g + k (token t, k-th head of the group in ascending order) below
 // cap = n_row_blocks * row_block. A group larger than the planned bound leaves its rows
 // r >= cap uncomputed, and a head whose map entry lies outside [0, G) belongs to no
-// group: the decode kernel never writes those (token, head) rows of `out`. This kernel
+// group: the decode kernel never writes those (token, head) rows of `out`. This routine
 // writes NaN into exactly those rows, so that `out` is always fully overwritten and a
 // bad map shows up in the result. One workgroup per (sequence, token): bt = b * q_len + t.
 // The persistent merge kernels run it in extra workgroups after their own; the split-K
@@ -213,7 +213,6 @@ __device__ __forceinline__ void fill_unmapped_rows(const DecodeParams& p, int d_
                                                           __builtin_nanf(""), __builtin_nanf("")});
   }
 }
-
 
 __global__ __launch_bounds__(kThreads) void fill_unmapped_rows_kernel(DecodeParams p, int d_h) {
   fill_unmapped_rows(p, d_h, blockIdx.x);
