@@ -178,3 +178,72 @@ def test_oversize_group_and_stray_entries_give_nan_rows(splits):
     for b in range(B):
         assert np.isnan(got[b][drop]).all()
         assert_parity(got[b][~drop], ref[b][~drop], "bfloat16", f"kept rows b={b}")
+
+
+def draw_map_case(seed):
+    """A seeded head-map case: sizes, a map with optional stray entries, an optional
+    group-size bound that may cut a group, an optional active mask."""
+    rng = np.random.default_rng(seed)
+    G = int(rng.choice([1, 2, 4, 6, 8, 16]))
+    H = int(rng.integers(G, 129))
+    q_len = int(rng.choice([1, 1, 2, 3, 4]))
+    d = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 9))
+    lens = [int(rng.integers(q_len, 3000)) for _ in range(B)]
+    page = int(rng.choice([0, 16, 32, 64]))
+    splits = int(rng.choice([0, 0, 1, 3, 9, 200]))
+    m = rng.integers(0, G, size=H).astype(np.int32)
+    if rng.random() < 0.3:
+        idx = rng.choice(H, size=min(int(rng.integers(1, 4)), H), replace=False)
+        m[idx] = rng.choice([-1, G, G + 3], size=len(idx))
+    counts = np.bincount(m[(m >= 0) & (m < G)], minlength=G)
+    maxh = int(rng.integers(1, counts.max() + 1)) if rng.random() < 0.4 and counts.max() > 1 else 0
+    active = (rng.random((B, q_len, H)) < 0.6).astype(np.uint8) if rng.random() < 0.3 else None
+    return B, H, G, d, q_len, lens, page, splits, m, maxh, active
+
+
+def packed_row_cap(H, q_len, maxh):
+    """Rows a group's packed tiles hold: the planner's row blocks for maxh (0 = H) heads."""
+    R = (H if maxh == 0 else maxh) * q_len
+    n_rb = 1 if R <= 256 else -(-R // 128)
+    rb = R if n_rb == 1 else (-(-R // n_rb) + 15) // 16 * 16
+    return n_rb * rb
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_head_map(seed):
+    """Random maps, stray entries, group-size bounds and active masks on random shapes,
+    through both merge forms: kept rows match the oracle, rows no packed tile holds are
+    NaN, and no row is left unwritten (out starts as a finite canary)."""
+    from gqa_kv_cache_03_amd import gqa_decode
+    B, H, G, d, q_len, lens, page, splits, m, maxh, active = draw_map_case(92000 + seed)
+    Hb = ((H + G - 1) // G) * G
+    wl, lens = small_workload(B, Hb, G, d, q_len, lens, paged=page, seed=92000 + seed)
+    inp = make(wl, lens)
+    inp.q = inp.q[:, :, :H].contiguous()
+    print(f"[variants] random map seed={seed} B={B} H={H} G={G} d={d} q_len={q_len} page={page} "
+          f"splits={splits} maxh={maxh} mask={active is not None}", flush=True)
+    out = torch.full_like(inp.q, 7.0)
+    kw = dict(head_group=torch.as_tensor(m, device="cuda"), max_group_heads=maxh)
+    if active is not None:
+        kw["head_active"] = torch.as_tensor(active, device="cuda")
+    gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table, scale=wl.scale, causal=wl.causal,
+               num_splits=splits, out=out, **kw)
+    torch.cuda.synchronize()
+    got = host64(out)
+    cap = packed_row_cap(H, q_len, maxh)
+    drop = np.zeros((q_len, H), dtype=bool)
+    for h in range(H):
+        g = int(m[h])
+        if not 0 <= g < G:
+            drop[:, h] = True
+            continue
+        members = [x for x in range(H) if m[x] == g]
+        k = members.index(h)
+        for t in range(q_len):
+            drop[t, h] = t * len(members) + k >= cap
+    safe = np.where((m >= 0) & (m < G), m, 0).astype(np.int32)
+    ref = oracle_variant(inp, head_group=safe, head_active=active)
+    for b in range(B):
+        assert np.isnan(got[b][drop]).all()
+        assert_parity(got[b][~drop], ref[b][~drop], "bfloat16", f"random map seed {seed} b={b}")
