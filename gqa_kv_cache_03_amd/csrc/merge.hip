@@ -140,35 +140,48 @@ __device__ __forceinline__ int tile_owner(int f, int W, int nwg) {
 }
 
 // GQLA absorbed execution, after the merge of a row's weighted latent u (512 values
-// in sm_u): out[row, i] = sum_c W_UV[gq][i, c] u[c], gq the row's query group. Each
-// output takes 256 / proj_dh threads, each a contiguous share of the columns with four
-// partial sums, added across the threads by lane swaps.
+// in sm_u): out[row, i] = sum_c W_UV[gq][i, c] u[c], gq the row's query group. A wave
+// takes eight outputs at a time: lane l works on output i0 + l / 8 and reads 16-byte
+// chunks (l % 8) + 8 s, s = 0..7, of that output's 1 KiB weight row, so every load
+// instruction covers eight whole 128-byte lines (one thread per output instead made
+// each load touch 64 lines). Each lane keeps the 64 values of u its chunks meet in
+// registers; the eight lanes of an output add their fp32 dot products by lane swaps.
 __device__ __forceinline__ void project_up(const DecodeParams& p, const float* sm_u, size_t orow, int h) {
   typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
   const int tid = threadIdx.x;
-  const int dh = p.proj_dh;              // 64 or 128
-  const int tpo = kThreads / dh;         // threads per output: 4 or 2
-  const int i = tid / tpo;
-  const int part = tid % tpo;
-  const int cols = 512 / tpo;            // 128 or 256
+  const int lane = tid & 63, wave = tid >> 6;
+  const int sub = lane & 7;    // chunk within each 128-byte line
+  const int oi = lane >> 3;    // output within the wave's eight
+  const int dh = p.proj_dh;    // 64 or 128
   const int gq = h / (p.H / p.proj_groups);
-  const __bf16* w = static_cast<const __bf16*>(p.w_uv) + ((size_t)gq * dh + i) * 512 + part * cols;
-  const float* u = sm_u + part * cols;
-  float a[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int cc = 0; cc < cols; cc += 8) {
-    const bf16x8 wv = *reinterpret_cast<const bf16x8*>(w + cc);
-    const f32x4 u0 = *reinterpret_cast<const f32x4*>(u + cc);
-    const f32x4 u1 = *reinterpret_cast<const f32x4*>(u + cc + 4);
+  const __bf16* w = static_cast<const __bf16*>(p.w_uv) + (size_t)gq * dh * 512;
+  f32x4 u[8][2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = __builtin_fmaf((float)wv[e], u0[e], a[e]);
-      a[e] = __builtin_fmaf((float)wv[4 + e], u1[e], a[e]);
-    }
+  for (int s = 0; s < 8; ++s) {
+    u[s][0] = *reinterpret_cast<const f32x4*>(sm_u + (sub + 8 * s) * 8);
+    u[s][1] = *reinterpret_cast<const f32x4*>(sm_u + (sub + 8 * s) * 8 + 4);
   }
-  float acc = (a[0] + a[1]) + (a[2] + a[3]);
-  for (int off = 1; off < tpo; off <<= 1) acc += __shfl_xor(acc, off);
-  if (part == 0) static_cast<__bf16*>(p.proj_out)[orow * dh + i] = (__bf16)acc;
+  // eight loads in flight per pass; issuing every pass's loads at once (208 instead
+  // of 126 registers) measured no faster
+  for (int i0 = wave * 8; i0 < dh; i0 += kThreads / 8) {
+    const __bf16* wrow = w + (size_t)(i0 + oi) * 512 + sub * 8;
+    bf16x8 wv[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) wv[s] = *reinterpret_cast<const bf16x8*>(wrow + s * 64);
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = __builtin_fmaf((float)wv[s][e], u[s][0][e], a[e]);
+        a[e] = __builtin_fmaf((float)wv[s][4 + e], u[s][1][e], a[e]);
+      }
+    float acc = (a[0] + a[1]) + (a[2] + a[3]);
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if (sub == 0) static_cast<__bf16*>(p.proj_out)[orow * dh + i0 + oi] = (__bf16)acc;
+  }
 }
 
 // With a call-time head -> KV head map, the packed tile of KV group g holds the rows
