@@ -29,6 +29,7 @@ constexpr size_t kWsAlign = 256;
 constexpr int kMfmaTile = 32;        // keys per tile of the persistent MFMA schedule
 constexpr int kDefaultCUs = 256;     // MI355X, used when no device can be queried
 constexpr int kWgsPerCu = 2;         // persistent workgroups per CU (fewer if fewer fit)
+constexpr double kMfmaMinCacheBytes = 16.0 * (1 << 20);  // K+V capacity from which bf16 R < 4 uses MFMA
 constexpr int kMaxDevices = 64;
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -139,8 +140,15 @@ int make_plan(int B, int H, int G, int d_h, int q_len, const gqa_decode_opts* op
   if (capacity < q_len) return GQA_ERR_INVALID_ARGUMENT;
 
   int policy = opts->policy;
-  if (policy == GQA_POLICY_AUTO)
-    policy = (opts->dtype == GQA_DTYPE_BF16 && (R >= 4 || variant || latent)) ? GQA_POLICY_MFMA : GQA_POLICY_VALU;
+  if (policy == GQA_POLICY_AUTO) {
+    // bf16 runs on the matrix cores from R = 4, and below that too once the cache is
+    // large enough (the persistent kernel then streams 10-33% faster than the vector
+    // kernel, whose one launch without a merge wins only on small caches)
+    const double cache_bytes = 4.0 * B * G * (double)capacity * d_h;
+    policy = (opts->dtype == GQA_DTYPE_BF16 && (R >= 4 || variant || latent || cache_bytes >= kMfmaMinCacheBytes))
+                 ? GQA_POLICY_MFMA
+                 : GQA_POLICY_VALU;
+  }
   if (policy == GQA_POLICY_MFMA && opts->dtype != GQA_DTYPE_BF16) return GQA_ERR_UNSUPPORTED;
 
   gqa_plan& pub = p.pub;

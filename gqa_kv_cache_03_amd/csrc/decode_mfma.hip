@@ -59,8 +59,10 @@ constexpr int kAhead = 1;
 template <int D, int NRW, int NCW, int RTW>
 struct MfmaCfg {
   static constexpr int T = kTile;
-  static constexpr int NS = kStages;
-  static constexpr int AHEAD = kAhead;
+  // A d_h = 64 tile is half the bytes: its ring keeps two tiles ahead in three stages,
+  // the same 32 KiB in flight per CU (measured 20-24% faster than one tile ahead).
+  static constexpr int NS = D == 64 ? 3 : kStages;
+  static constexpr int AHEAD = D == 64 ? 2 : kAhead;
   static_assert(AHEAD >= 1 && AHEAD < NS, "a tile is refilled only after every wave has consumed it");
   static constexpr int KB = T / 16;           // 16-key blocks per tile
   static constexpr int CC = D / 32;           // k-steps of QK^T

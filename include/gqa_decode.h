@@ -63,8 +63,10 @@ typedef enum gqa_status {
 typedef enum gqa_dtype { GQA_DTYPE_F32 = 0, GQA_DTYPE_BF16 = 1 } gqa_dtype;
 
 /* Inner-product policy. AUTO: bf16 groups of R >= 4 packed query rows run QK^T and PV
- * on MFMA (the packed rows make them dense contractions), everything else on the
- * vector ALUs. The other values force one policy (tests, measurement). */
+ * on MFMA (the packed rows make them dense contractions), and so do bf16 groups of
+ * fewer rows once the cache (B * G * capacity * d_h K and V elements) holds 16 MiB or
+ * more; fp32, and small bf16 caches below R = 4, run on the vector ALUs. The other
+ * values force one policy (tests, measurement). */
 typedef enum gqa_policy { GQA_POLICY_AUTO = 0, GQA_POLICY_VALU = 1, GQA_POLICY_MFMA = 2 } gqa_policy;
 
 typedef struct gqa_decode_opts {

@@ -188,11 +188,27 @@ def test_persistent_default_fills_the_device():
 def test_every_row_count_up_to_the_maximum_plans(R):
     st, pl = plan(H=R, G=1, q_len=1, o=opts(cache_capacity=1 << 16))
     assert st == OK and pl.rows == R
-    assert pl.policy == (_lib.GQA_POLICY_MFMA if R >= 4 else _lib.GQA_POLICY_VALU)
+    # a 64 MiB K+V cache: the matrix cores at any R (below R = 4 only from 16 MiB on)
+    assert pl.policy == _lib.GQA_POLICY_MFMA
     assert pl.lds_bytes <= 160 * 1024
     if pl.policy == _lib.GQA_POLICY_MFMA:
         # one block up to 256 rows; a larger group in blocks of at most 128 rows
         assert pl.row_blocks == (1 if R <= 256 else -(-R // 128))
+
+
+@pytest.mark.parametrize("R", [1, 2, 3])
+def test_small_row_counts_take_the_matrix_cores_from_16_mib_of_cache(R):
+    # K+V capacity bytes = 2 * 2 * B * G * capacity * d_h; the threshold is 16 MiB
+    B, G, d = 2, 8, 128
+    cap_at = (16 << 20) // (4 * B * G * d)          # exactly 16 MiB
+    for cap, want in ((cap_at - 1, _lib.GQA_POLICY_VALU), (cap_at, _lib.GQA_POLICY_MFMA)):
+        st, pl = plan(B=B, H=G * R, G=G, d=d, q_len=1, o=opts(cache_capacity=cap))
+        assert st == OK and pl.rows == R and pl.policy == want, (cap, pl.policy)
+    # fp32 always on the vector ALUs; R >= 4 always on the matrix cores
+    st, pl = plan(B=B, H=G * R, G=G, d=d, q_len=1, o=opts(cache_capacity=cap_at, dtype=_lib.GQA_DTYPE_F32))
+    assert pl.policy == _lib.GQA_POLICY_VALU
+    st, pl = plan(B=B, H=G * 4, G=G, d=d, q_len=1, o=opts(cache_capacity=16))
+    assert pl.policy == _lib.GQA_POLICY_MFMA
 
 
 def test_status_strings():
