@@ -321,3 +321,24 @@ def test_merge_forms(B, H, G, d, q_len, lens, nwg, form):
     print(f"[parity] merge form {form}: B={B} H={H} G={G} d={d} q_len={q_len} nwg={nwg}", flush=True)
     got = run(inp, num_splits=nwg)
     assert_parity(got, oracle_for(inp), "bfloat16", f"{form} form nwg={nwg}")
+
+
+@pytest.mark.parametrize("H,G,d,q_len,page", [(8, 8, 128, 1, 0), (16, 8, 128, 1, 16), (24, 8, 128, 1, 0),
+                                              (8, 8, 128, 3, 32), (8, 8, 64, 2, 0), (24, 8, 64, 1, 16)])
+def test_small_row_counts_on_a_large_cache_take_the_matrix_cores(H, G, d, q_len, page):
+    """Fewer than 4 packed rows over a cache of 16 MiB or more: AUTO picks the persistent
+    matrix-core kernel, whose 16-row tiles then hold 13-15 padding rows; every unit still
+    matches the oracle."""
+    from gqa_kv_cache_03_amd import gqa_decode, plan
+    from gpu_cases import all_units_parity
+    lens = [20000, 9000 + q_len, 16384, 33]
+    wl, lens = small_workload(4, H, G, d, q_len, lens, paged=page, seed=8800 + H + d + q_len)
+    inp = make(wl, lens)
+    pl = plan(inp.q, inp.k_cache, inp.block_table, causal=wl.causal)
+    assert pl["policy"] == "mfma" and pl["rows"] == H // G * q_len < 4, pl
+    print(f"[small R] H={H} G={G} d={d} q_len={q_len} page={page} R={pl['rows']}", flush=True)
+    out = gqa_decode(inp.q, inp.k_cache, inp.v_cache, inp.seq_lens, inp.block_table, scale=wl.scale,
+                     causal=wl.causal)
+    torch.cuda.synchronize()
+    worst = all_units_parity(inp, out, f"small R H={H} G={G} d={d} q_len={q_len}", log=lambda m: None)
+    assert worst["units"] == wl.B * wl.G
