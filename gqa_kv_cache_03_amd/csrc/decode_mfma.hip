@@ -21,8 +21,10 @@
 // tiles held in registers (a group of more than 256 rows is split into row blocks of
 // at most 128, each a segment of its own). K/V rows stream from HBM exactly once per
 // row block (the aiwiki note after the listing: the cache is read once, not copied per
-// head) through a double-buffered LDS ring filled by direct global->LDS loads
-// (nontemporal, 16 bytes per lane); the ring keeps running across segment boundaries.
+// head) through an LDS ring (two stages; three at d_h = 64) filled by direct
+// global->LDS loads (16 bytes per lane; nontemporal unless the group is split into row
+// blocks, whose repeated reads L2 then serves); the ring keeps running across segment
+// boundaries.
 // Every packed row consumes each staged tile, i.e. the H/G-fold broadcast happens in
 // registers, never in memory.
 //
@@ -52,7 +54,7 @@ constexpr int kThreads = 256;
 // LDS ring depth and the number of tiles issued ahead of the one being consumed
 // (< kStages). Measured on MI355X with two workgroups per CU: one tile ahead (32 KiB
 // of K/V in flight per CU) streams faster than two or three, on every workload
-// shape here, so the ring is a double buffer.
+// shape here at d_h = 128, so the ring is a double buffer there (d_h = 64: see MfmaCfg).
 constexpr int kStages = 2;
 constexpr int kAhead = 1;
 
@@ -294,7 +296,7 @@ __device__ __forceinline__ void decode_mfma_body(DecodeParams p) {
 
   // Writes the new tokens' rows of staged tile f (already in LDS: every lane reads
   // back the chunks its own loads placed) into the cache. Called right after the
-  // tile's wait, while nothing else is in flight.
+  // tile's wait, which its own loads have passed (later tiles may still be loading).
   auto copy_new_rows = [&](const Cursor& c, int f) {
     // every row block of a group stages the same tile; the first one writes it (the
     // latent is one tensor: its new rows go to the one cache)
@@ -721,7 +723,7 @@ __device__ __forceinline__ void decode_mfma_body(DecodeParams p) {
       wait_tiles<LD, AHEAD - 1>(count - 1 - f);  // tiles issued after this one: min(AHEAD - 1, .)
     }
     // new tokens' rows of this tile go to the cache before the next tile is issued,
-    // so their LDS read-back waits for nothing else
+    // so their LDS read-back needs no wait beyond the tile's own
     copy_new_rows(cons, f);
     // the stage refilled next was last read at step f + AHEAD - NS <= f - 1, which
     // every wave has finished (the barrier above)
